@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of one LoPA branch-verification step on one MI355X.
+
+A step = lopa_branch_build -> lopa_branch_attn -> lopa_lmhead_conf ->
+lopa_branch_select on one batch of seeded synthetic inputs already resident
+in HBM, enqueued on one stream.  Default workload: 7B D2F-Dream-like shapes
+(28 q-heads / 4 kv-heads / d 128, hidden 3584, vocabulary 152064, bf16),
+committed prefix 512, block 32 with 24 masked positions, k = 4 (5 branches).
+
+Prints ONE JSON line: verification steps/s (value), branch-tokens/s, the
+LM-head call's roofline (algorithmic bytes per call / its HIP-event-timed
+duration vs 8 TB/s) and the CPU oracle timed on a bounded sample on this
+host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: prefix 512, k=4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="lower bound on the oracle's timed CPU work")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, nb: int, M: int) -> dict:
+    """Bytes and flops one step must move / do (each input read once, each
+    output written once), with nb live branches and M LM-head rows."""
+    e = 4 if cfg.dtype == "f32" else 2
+    hid = cfg.hidden
+    w = cfg.V * hid * e
+    head_bytes = w + M * hid * e + M * 8                     # W, H rows, conf+arg
+    attn_bytes = (2 * cfg.L * cfg.Hkv * cfg.d + nb * cfg.B * (cfg.Hq + 2 * cfg.Hkv) * cfg.d) * e \
+        + nb * cfg.B * hid * e                               # prefix K/V, Q/K/V, H write
+    small = cfg.B * 12 + nb * cfg.B * 9 + cfg.B * 12         # build/select state
+    head_flops = 2.0 * M * hid * cfg.V
+    attn_flops = 4.0 * nb * cfg.B * cfg.Hq * (cfg.L + cfg.B) * cfg.d
+    return dict(step_bytes=head_bytes + attn_bytes + small, head_bytes=head_bytes,
+                attn_bytes=attn_bytes, head_flops=head_flops, attn_flops=attn_flops,
+                w_bytes=w)
+
+
+def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.verification_step(inp, conf, arg)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 50:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full oracle step(s) of the same workload (build, per-branch fp64 "
+                      f"attention, fp64 LM head over all {inp.cfg.V} entries of every listed row, "
+                      f"select) in {el:.1f} s; cores = BLAS threads of the fp64 matmul"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the step is not "
+              "sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lookahead_decoding_amd as lopa
+    import synth
+    from lookahead_decoding_amd.step import StepBuffers, dims_of, initial_pass, run_step, to_device
+
+    name = args.workload or synth.HEADLINE
+    inp = synth.make_inputs(name)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    torch.cuda.set_device(0)
+    lopa.lib()
+    stream = torch.cuda.current_stream()
+    x = {k: to_device(v) for k, v in inp.arrays().items()}
+    buf = StepBuffers(dims)
+    conf0, arg0 = initial_pass(dims, inp.tok, x, buf)
+    x["conf"], x["arg"] = conf0, arg0
+    torch.cuda.synchronize()
+
+    # one step to learn nb and M (state is fixed, so every step is identical)
+    run_step(dims, cfg.k, cfg.tau, x, buf)
+    torch.cuda.synchronize()
+    nb = int(buf.nb.item())
+    M = int(buf.row_ptr[nb].item())
+    alg = algorithmic(cfg, nb, M)
+
+    def step():
+        run_step(dims, cfg.k, cfg.tau, x, buf)
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay() if graph else step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay() if graph else step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el / args.steps * 1e3
+
+    # Per-call durations with HIP events on the stream the calls run on.
+    K = max(20, min(args.steps, 100))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        lopa.lopa_branch_build(dims, cfg.k, cfg.tau, x["tok"], x["conf"], x["arg"], buf.nb,
+                               buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr)
+        e[1].record(stream)
+        lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H)
+        e[2].record(stream)
+        lopa.lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
+                              buf.arg, None, buf.ws)
+        e[3].record(stream)
+        lopa.lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg,
+                                buf.bconf, buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
+    call_us = per.mean(axis=0) * 1e3
+    head_us = float(call_us[2])
+    achieved = alg["head_bytes"] / (head_us * 1e-6) / 1e9
+
+    steps_s = 1e3 / ms
+    out = {
+        "metric": "LoPA verification steps/s (7B shapes, 1 GPU)",
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random Q/K/V and LM-head weight of 7B shape)",
+        "config": {"workload": cfg.name, "L": cfg.L, "B": cfg.B, "masked": cfg.m, "k": cfg.k,
+                   "branches": nb, "lmhead_rows": M, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "hidden": cfg.hidden, "V": cfg.V, "tau": cfg.tau,
+                   "graph": bool(args.graph)},
+        "branch_tokens_per_s": round(steps_s * nb * cfg.B, 1),
+        "lmhead_rows_per_s": round(steps_s * M, 1),
+        "step_hbm_frac": round(alg["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round((alg["head_flops"] + alg["attn_flops"]) / (ms * 1e-3) / 1e12
+                                / BF16_PEAK_TFLOPS, 4),
+        "call_us": {"branch_build": round(float(call_us[0]), 2),
+                    "branch_attn": round(float(call_us[1]), 2),
+                    "lmhead_conf": round(float(call_us[2]), 2),
+                    "branch_select": round(float(call_us[3]), 2)},
+        "roofline": {"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_call": alg["head_bytes"],
+                     "mfma_tflops": round(alg["head_flops"] / (head_us * 1e-6) / 1e12, 1)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O  # noqa: F401  (CPU baseline leg only)
+        c, a, _ = O.initial_state(inp)
+        out["cpu_baseline"] = cpu_baseline(inp, c, a, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

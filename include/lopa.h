@@ -1,0 +1,177 @@
+/*
+ * lopa.h -- C ABI of liblopa, the MI355X (gfx950) library for one LoPA
+ * branch-verification step (Lookahead Parallel Decoding for diffusion LLMs).
+ *
+ * One step, in the order the method states it:
+ *   1. lopa_branch_build  -- explore: the anchor branch (confidence-driven
+ *      fill) plus k lookahead branches, each filling one more of the most
+ *      confident positions the anchor left masked.
+ *      ["上交大 × 华为小艺推出LoPA：7B扩散语言模型单样例1000+ tokens/s！",
+ *       section "LoPA 的核心设计：前瞻并行与分支验证", stage 多分支并行探索;
+ *       "解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈", section 3.1]
+ *   2. lopa_branch_attn   -- verify, attention part: every branch attends to
+ *      the shared committed prefix and to its own block only; all branches in
+ *      one pass.  ["解码效率革命…", section 3.3; same article section 6 for
+ *      full-sequence (bidirectional) attention; news article, stage 并行验证与复用]
+ *   3. lopa_lmhead_conf   -- verify, LM-head part: per still-masked (branch,
+ *      position) the largest softmax probability over the vocabulary (the
+ *      position's confidence) and its argmax token, without storing logits.
+ *      [news article, stages 分支置信度验证 and 并行验证与复用]
+ *   4. lopa_branch_select -- branch confidence = mean confidence over the
+ *      branch's still-masked positions; the highest wins and its per-position
+ *      (confidence, token) become the next step's state (reuse).
+ *      [news article, stages 分支置信度验证 and 并行验证与复用;
+ *       "LoPA：上海交大與華為聯手破解AI推理新困境", third stage]
+ *
+ * Conventions shared by every call:
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or keeps one.  `dims` is a HOST pointer read
+ *     during the call only.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *     synchronise with the host.  The live branch count nb and the LM-head row
+ *     count M stay on the device; launch grids are sized for nb_max = 1+k_max.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     negative lopa_status is returned and nothing is launched.  A failed
+ *     launch returns LOPA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Stateless and thread-safe; calls that share a workspace must be ordered
+ *     (the same stream orders them).
+ *   - Layouts are dense row-major as annotated.  Activations (Q, K, V, H, W)
+ *     are all of dims->dtype: IEEE float32, or bfloat16 (raw 16-bit patterns).
+ *   - Per-position arrays of all branches are indexed b*B + p (branch b,
+ *     block position p).  The mask token id is LOPA_MASK_TOKEN.
+ */
+#ifndef LOPA_H
+#define LOPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOPA_ABI_VERSION 1
+#define LOPA_MASK_TOKEN (-1)
+#define LOPA_MAX_BLOCK 64        /* B <= 64: one block fits one wavefront      */
+#define LOPA_MAX_BRANCHES 16     /* nb_max = 1 + k_max <= 16                   */
+
+typedef enum {
+  LOPA_OK = 0,
+  LOPA_ERR_INVALID = -1,      /* null pointer, bad size, k > k_max, ...        */
+  LOPA_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle     */
+  LOPA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
+  LOPA_ERR_HIP = -4           /* the HIP runtime rejected a launch             */
+} lopa_status;
+
+typedef enum { LOPA_F32 = 0, LOPA_BF16 = 1 } lopa_dtype;
+
+/* Shape of a step.  hidden = Hq * d is the LM-head contraction length. */
+typedef struct lopa_dims {
+  int32_t L;      /* committed prefix length shared by all branches, >= 0     */
+  int32_t B;      /* block length, 1..64                                      */
+  int32_t Hq;     /* query heads                                              */
+  int32_t Hkv;    /* key/value heads, Hq % Hkv == 0 (grouped-query attention) */
+  int32_t d;      /* head dimension, 1..256                                   */
+  int32_t V;      /* vocabulary size, >= 1                                    */
+  int32_t k_max;  /* largest lookahead count any call will use, 0..15         */
+  int32_t dtype;  /* lopa_dtype of all activations                            */
+} lopa_dims;
+
+/* LOPA_ABI_VERSION of the built library. */
+int lopa_abi_version(void);
+
+/* Static English text for a lopa_status value (never NULL). */
+const char* lopa_status_string(int status);
+
+/* Bytes of device workspace lopa_lmhead_conf needs for these dims (written to
+ * *bytes).  Returns LOPA_OK or LOPA_ERR_INVALID.  Pure host computation. */
+int lopa_workspace_bytes(const lopa_dims* dims, size_t* bytes);
+
+/*
+ * Explore: build the anchor branch and up to k lookahead branches.
+ *
+ * In  tok[B]  int32  block tokens, LOPA_MASK_TOKEN where masked
+ *     conf[B] float  confidence of each masked position (previous step)
+ *     arg[B]  int32  predicted token of each masked position
+ *     k       lookahead count, 0 <= k <= dims->k_max
+ *     tau     fill threshold: the anchor fills every masked p with conf > tau
+ *             (strict); if there is none, the single most confident masked p
+ *             (lowest p on a tie).  The lookahead positions are the
+ *             k_eff = min(k, #left masked) most confident positions the anchor
+ *             left masked (confidence descending, position ascending); branch
+ *             j fills the anchor's positions plus the j-th of them.  A filled
+ *             position takes arg[p].
+ * Out nb[1]                 int32  1 + k_eff
+ *     br_tok[nb_max*B]      int32  tokens of each branch
+ *     br_mask[nb_max*B]     uint8  1 where the branch leaves p masked
+ *     rows[nb_max*B]        int32  b*B+p of every still-masked pair, branch-
+ *                                  major, p ascending; M = row_ptr[nb] entries
+ *     row_ptr[nb_max+1]     int32  rows of branch b are [row_ptr[b], row_ptr[b+1])
+ *     Slots b >= nb get the anchor's tokens, an all-zero mask and no rows.
+ * Bit-exact integer/compare logic; one wavefront.
+ */
+int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
+                      const int32_t* tok, const float* conf, const int32_t* arg,
+                      int32_t* nb, int32_t* br_tok, uint8_t* br_mask,
+                      int32_t* rows, int32_t* row_ptr, hipStream_t stream);
+
+/*
+ * Verify, attention: for branch b < nb, position i < B, query head h with
+ * key/value head g = h / (Hq/Hkv):
+ *   H[b][i][h*d : h*d+d] = sum_j softmax_j(Q_b,i,h . K_j / sqrt(d)) V_j
+ * over keys j = the L prefix keys (Kp/Vp, shared) followed by branch b's own
+ * B block keys (Kb/Vb[b]); bidirectional inside the block, other branches'
+ * blocks never visible.  The isolation is computed from indices; no mask is
+ * stored.
+ * In  Kp, Vp [L][Hkv][d];  Qb [nb_max][B][Hq][d];  Kb, Vb [nb_max][B][Hkv][d]
+ *     nb[1] (device)
+ * Out H [nb_max][B][Hq*d], rounded once to dtype (bf16: nearest-even).
+ *     Slots b >= nb are not written.
+ * Accumulation and softmax in float32.
+ */
+int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const void* Vp,
+                     const void* Qb, const void* Kb, const void* Vb,
+                     const int32_t* nb, void* H, hipStream_t stream);
+
+/*
+ * Verify, LM head: for every listed row r = rows[m] (m < M = row_ptr[nb]),
+ * logits l_v = sum_k H[r][k] * W[v][k] (v < V), and
+ *   arg[r]  = lowest v attaining max_v l_v
+ *   conf[r] = 1 / sum_v exp(l_v - max l)   (the largest softmax probability)
+ * computed in one streaming pass over W with an online (max, sum, argmax)
+ * merge; logits are not stored unless logits_out is given.
+ * In  H [nb_max][B][Hq*d];  W [V][Hq*d] (vocabulary-major);  rows, row_ptr, nb
+ *     as written by lopa_branch_build
+ * Out conf[nb_max*B] float, arg[nb_max*B] int32 -- only listed entries written
+ *     logits_out  NULL, or float [nb_max*B][V] indexed like H rows (b*B+p);
+ *                 only listed rows written
+ *     ws, ws_bytes  device workspace of at least lopa_workspace_bytes()
+ * bf16: MFMA products with float32 accumulation; float32: FMA.
+ */
+int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
+                     const int32_t* rows, const int32_t* row_ptr,
+                     const int32_t* nb, float* conf, int32_t* arg,
+                     float* logits_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Select and reuse: branch confidence bconf[b] = mean of conf[b*B+p] over
+ * the p with br_mask[b*B+p] = 1 (1.0 when there is none), for b < nb;
+ * bconf[b] = -1 for b >= nb.  winner = the first b with the largest bconf
+ * (the anchor wins ties).  Next state: tok_next = br_tok[winner]; where the
+ * winner is still masked conf_next/arg_next = its conf/arg, elsewhere 0 / -1.
+ * In  nb[1], br_mask, br_tok, conf, arg  (as written by the calls above)
+ * Out bconf[nb_max] float, winner[1] int32, tok_next[B], conf_next[B],
+ *     arg_next[B].  float32 sums; one wavefront.
+ */
+int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
+                       const uint8_t* br_mask, const int32_t* br_tok,
+                       const float* conf, const int32_t* arg,
+                       float* bconf, int32_t* winner, int32_t* tok_next,
+                       float* conf_next, int32_t* arg_next, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOPA_H */

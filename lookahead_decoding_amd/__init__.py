@@ -1,0 +1,181 @@
+"""Python binding of liblopa: one LoPA branch-verification step on MI355X.
+
+Argument marshalling only.  Every function below forwards torch device
+tensors (as raw pointers) and sizes to the C ABI declared in
+``include/lopa.h``; all of the step's arithmetic runs in the library's HIP
+kernels.  There is no CPU fallback: if ``liblopa.so`` is missing the import of
+the library raises.
+
+    import lookahead_decoding_amd as lopa
+    dims = lopa.Dims(L=512, B=32, Hq=28, Hkv=4, d=128, V=152064, k_max=4,
+                     dtype=lopa.BF16)
+    lopa.lopa_branch_build(dims, k, tau, tok, conf, arg, nb, br_tok, br_mask,
+                           rows, row_ptr)
+    ...
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblopa.so")
+
+F32 = 0
+BF16 = 1
+MASK = -1
+MAX_BLOCK = 64
+MAX_BRANCHES = 16
+
+STATUS = {0: "LOPA_OK", -1: "LOPA_ERR_INVALID", -2: "LOPA_ERR_UNSUPPORTED",
+          -3: "LOPA_ERR_WORKSPACE", -4: "LOPA_ERR_HIP"}
+
+
+class Dims(ctypes.Structure):
+    """Mirror of ``lopa_dims``."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("L", "B", "Hq", "Hkv", "d", "V", "k_max", "dtype")]
+
+    @property
+    def hidden(self) -> int:
+        return self.Hq * self.d
+
+    @property
+    def nb_max(self) -> int:
+        return self.k_max + 1
+
+    def __repr__(self) -> str:
+        return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class LopaError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+_SIGS = {
+    "lopa_abi_version": ([], ctypes.c_int),
+    "lopa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "lopa_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "lopa_branch_build": ([ctypes.POINTER(Dims), _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                          ctypes.c_int),
+    "lopa_branch_attn": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "lopa_lmhead_conf": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                         ctypes.c_int),
+    "lopa_branch_select": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                           ctypes.c_int),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded liblopa (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LopaError(fn, status, lib().lopa_status_string(status).decode())
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Raw device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _act_dtype(dims):
+    import torch
+    return torch.float32 if dims.dtype == F32 else torch.bfloat16
+
+
+def abi_version() -> int:
+    return lib().lopa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().lopa_status_string(status).decode()
+
+
+def workspace_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lopa_workspace_bytes", lib().lopa_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def lopa_branch_build(dims, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows, row_ptr,
+                      stream=None) -> None:
+    import torch
+    i32, f32, u8 = torch.int32, torch.float32, torch.uint8
+    _check("lopa_branch_build", lib().lopa_branch_build(
+        ctypes.byref(dims), int(k), float(tau),
+        _ptr(tok, i32, "tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
+        _ptr(nb, i32, "nb"), _ptr(br_tok, i32, "br_tok"), _ptr(br_mask, u8, "br_mask"),
+        _ptr(rows, i32, "rows"), _ptr(row_ptr, i32, "row_ptr"), _stream(stream)))
+
+
+def lopa_branch_attn(dims, Kp, Vp, Qb, Kb, Vb, nb, H, stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    _check("lopa_branch_attn", lib().lopa_branch_attn(
+        ctypes.byref(dims), _ptr(Kp, a, "Kp"), _ptr(Vp, a, "Vp"), _ptr(Qb, a, "Qb"),
+        _ptr(Kb, a, "Kb"), _ptr(Vb, a, "Vb"), _ptr(nb, torch.int32, "nb"), _ptr(H, a, "H"),
+        _stream(stream)))
+
+
+def lopa_lmhead_conf(dims, H, W, rows, row_ptr, nb, conf, arg, logits_out, ws,
+                     stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    i32 = torch.int32
+    _check("lopa_lmhead_conf", lib().lopa_lmhead_conf(
+        ctypes.byref(dims), _ptr(H, a, "H"), _ptr(W, a, "W"), _ptr(rows, i32, "rows"),
+        _ptr(row_ptr, i32, "row_ptr"), _ptr(nb, i32, "nb"), _ptr(conf, torch.float32, "conf"),
+        _ptr(arg, i32, "arg"), _ptr(logits_out, torch.float32, "logits_out"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def lopa_branch_select(dims, nb, br_mask, br_tok, conf, arg, bconf, winner, tok_next,
+                       conf_next, arg_next, stream=None) -> None:
+    import torch
+    i32, f32 = torch.int32, torch.float32
+    _check("lopa_branch_select", lib().lopa_branch_select(
+        ctypes.byref(dims), _ptr(nb, i32, "nb"), _ptr(br_mask, torch.uint8, "br_mask"),
+        _ptr(br_tok, i32, "br_tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
+        _ptr(bconf, f32, "bconf"), _ptr(winner, i32, "winner"), _ptr(tok_next, i32, "tok_next"),
+        _ptr(conf_next, f32, "conf_next"), _ptr(arg_next, i32, "arg_next"), _stream(stream)))
+
+
+from .step import StepBuffers, run_step, initial_pass  # noqa: E402,F401

@@ -1,0 +1,164 @@
+// Explore and select stages of one LoPA step.  Each is one wavefront: lane p
+// owns block position p (B <= 64), so the whole stage is ballots, shuffles
+// and one coalesced store per array.
+//
+// Explore follows the news article "上交大 × 华为小艺推出LoPA：7B扩散语言模型单样例
+// 1000+ tokens/s！", section "LoPA 的核心设计：前瞻并行与分支验证", stage
+// 多分支并行探索 (anchor = ordinary greedy fill, plus k branches that each also
+// fill one of the currently most confident positions), and section 3.1 of
+// "解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈".
+// Select follows the same news section, stages 分支置信度验证 (branch
+// confidence = mean confidence of the positions a branch leaves unfilled) and
+// 并行验证与复用 (the best branch is kept and its verification outputs seed
+// the next step).
+#include "lopa_common.hpp"
+
+namespace lopa {
+
+__global__ void __launch_bounds__(64)
+k_branch_build(int B, int nb_max, int k, float tau,
+               const int32_t* __restrict__ tok, const float* __restrict__ conf,
+               const int32_t* __restrict__ arg, int32_t* __restrict__ nb_out,
+               int32_t* __restrict__ br_tok, uint8_t* __restrict__ br_mask,
+               int32_t* __restrict__ rows, int32_t* __restrict__ row_ptr) {
+  const int p = threadIdx.x;
+  const bool live = p < B;
+  const int t = live ? tok[p] : 0;
+  const float c = live ? conf[p] : 0.f;
+  const int a = live ? arg[p] : 0;
+  const bool masked = live && t == LOPA_MASK_TOKEN;
+
+  // Anchor: every masked position strictly above tau ...
+  bool fill = masked && c > tau;
+  const unsigned long long any_masked = __ballot(masked);
+  if (__ballot(fill) == 0ull && any_masked != 0ull) {
+    // ... else the single most confident masked position (lowest p on a tie).
+    float bv = masked ? c : 0.f;
+    int bi = masked ? p : 0x7fffffff;
+    bool bok = masked;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const bool ook = __shfl_xor(static_cast<int>(bok), o, kWave) != 0;
+      if (ook && (!bok || better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+        bok = true;
+      }
+    }
+    fill = (p == bi);
+  }
+  const bool remaining = masked && !fill;
+  const unsigned long long rem_bits = __ballot(remaining);
+  const int n_rem = __popcll(rem_bits);
+
+  // Rank of each remaining position by (confidence desc, position asc).
+  int rank = 0;
+  for (int q = 0; q < B; ++q) {
+    const float cq = __shfl(c, q, kWave);
+    if (((rem_bits >> q) & 1ull) && (cq > c || (cq == c && q < p))) ++rank;
+  }
+  const int k_eff = k < n_rem ? k : n_rem;
+  const int nb = 1 + k_eff;
+  const int my_branch = (remaining && rank < k_eff) ? rank + 1 : 0;  // 0: not a lookahead pos
+
+  const int anchor_tok = fill ? a : t;
+  // index of p among the remaining positions (ascending p)
+  const unsigned long long below = (p == 0) ? 0ull : (~0ull >> (64 - p));
+  const int idx_rem = __popcll(rem_bits & below);
+
+  for (int b = 0; b < nb_max; ++b) {
+    const bool in_use = b < nb;
+    const int tb = (in_use && b >= 1 && my_branch == b) ? a : anchor_tok;
+    const bool mb = in_use && tb == LOPA_MASK_TOKEN;
+    // lookahead position of this branch, to drop it from the row list
+    int qb = -1;
+    if (b >= 1 && in_use) {
+      const unsigned long long qbits = __ballot(my_branch == b);
+      qb = __ffsll(static_cast<long long>(qbits)) - 1;
+    }
+    if (live) {
+      br_tok[b * B + p] = tb;
+      br_mask[b * B + p] = mb ? 1 : 0;
+    }
+    const int start = (b == 0) ? 0 : (b <= nb ? n_rem + (b - 1) * (n_rem - 1)
+                                              : n_rem + (nb - 1) * (n_rem - 1));
+    if (mb) rows[start + idx_rem - ((qb >= 0 && p > qb) ? 1 : 0)] = b * B + p;
+    if (p == 0) row_ptr[b] = start;
+  }
+  if (p == 0) {
+    row_ptr[nb_max] = n_rem == 0 ? 0 : n_rem + (nb - 1) * (n_rem - 1);
+    nb_out[0] = nb;
+  }
+}
+
+__global__ void __launch_bounds__(64)
+k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
+                const uint8_t* __restrict__ br_mask, const int32_t* __restrict__ br_tok,
+                const float* __restrict__ conf, const int32_t* __restrict__ arg,
+                float* __restrict__ bconf, int32_t* __restrict__ winner,
+                int32_t* __restrict__ tok_next, float* __restrict__ conf_next,
+                int32_t* __restrict__ arg_next) {
+  const int p = threadIdx.x;
+  const bool live = p < B;
+  const int nb = *nb_ptr;
+  float best = 0.f;
+  int w = 0;
+  for (int b = 0; b < nb_max; ++b) {
+    float bc = -1.f;
+    if (b < nb) {
+      const bool m = live && br_mask[b * B + p] != 0;
+      const float s = wave_sum(m ? conf[b * B + p] : 0.f);
+      const int n = __popcll(__ballot(m));
+      bc = n ? s / static_cast<float>(n) : 1.f;
+      if (b == 0 || bc > best) {
+        best = bc;
+        w = b;
+      }
+    }
+    if (p == 0) bconf[b] = bc;
+  }
+  if (live) {
+    const bool m = br_mask[w * B + p] != 0;
+    tok_next[p] = br_tok[w * B + p];
+    conf_next[p] = m ? conf[w * B + p] : 0.f;
+    arg_next[p] = m ? arg[w * B + p] : -1;
+  }
+  if (p == 0) winner[0] = w;
+}
+
+}  // namespace lopa
+
+extern "C" int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
+                                 const int32_t* tok, const float* conf, const int32_t* arg,
+                                 int32_t* nb, int32_t* br_tok, uint8_t* br_mask,
+                                 int32_t* rows, int32_t* row_ptr, hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (k < 0 || k > dims->k_max) return LOPA_ERR_INVALID;
+  if (!tok || !conf || !arg || !nb || !br_tok || !br_mask || !rows || !row_ptr)
+    return LOPA_ERR_INVALID;
+  hipLaunchKernelGGL(lopa::k_branch_build, dim3(1), dim3(64), 0, stream, dims->B,
+                     dims->k_max + 1, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows,
+                     row_ptr);
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}
+
+extern "C" int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
+                                  const uint8_t* br_mask, const int32_t* br_tok,
+                                  const float* conf, const int32_t* arg, float* bconf,
+                                  int32_t* winner, int32_t* tok_next, float* conf_next,
+                                  int32_t* arg_next, hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (!nb || !br_mask || !br_tok || !conf || !arg || !bconf || !winner || !tok_next ||
+      !conf_next || !arg_next)
+    return LOPA_ERR_INVALID;
+  hipLaunchKernelGGL(lopa::k_branch_select, dim3(1), dim3(64), 0, stream, dims->B,
+                     dims->k_max + 1, nb, br_mask, br_tok, conf, arg, bconf, winner,
+                     tok_next, conf_next, arg_next);
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}

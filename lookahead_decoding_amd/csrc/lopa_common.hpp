@@ -1,0 +1,120 @@
+// Internal helpers shared by liblopa's kernels and entry points.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 with float32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lopa.h"
+
+namespace lopa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short u) {
+  return __uint_as_float(static_cast<unsigned>(u) << 16);
+}
+
+// float -> bf16 bit pattern, round to nearest, ties to even (finite inputs;
+// NaN maps to a quiet NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<unsigned short>(u >> 16);
+}
+
+template <typename T> struct Act;
+template <> struct Act<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Act<unsigned short> {
+  static __device__ __forceinline__ float load(const unsigned short* p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void store(unsigned short* p, size_t i, float v) {
+    p[i] = f32_to_bf16_bits(v);
+  }
+};
+
+// (max, index) pair ordering used by every argmax here: larger value wins,
+// the lower index wins an exact tie.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Online-softmax partial over a set of logits l: m = max l, s = sum
+// exp(l - m), i = lowest index attaining m.  The empty partial has s == 0.
+struct Partial {
+  float m;
+  float s;
+  int i;
+};
+
+__device__ __forceinline__ Partial empty_partial() { return Partial{-INFINITY, 0.f, 0x7fffffff}; }
+
+// Merge of two partials over disjoint index sets; exact in (m, i), and the
+// sums are rescaled to the larger max.
+__device__ __forceinline__ Partial merge(Partial a, Partial b) {
+  if (b.s == 0.f) return a;
+  if (a.s == 0.f) return b;
+  Partial r;
+  if (better(b.m, b.i, a.m, a.i)) {
+    r.m = b.m;
+    r.i = b.i;
+  } else {
+    r.m = a.m;
+    r.i = a.i;
+  }
+  r.s = a.s * exp2f((a.m - r.m) * kLog2e) + b.s * exp2f((b.m - r.m) * kLog2e);
+  return r;
+}
+
+// Rows listed for the LM head, from the device-side branch count; both are
+// clamped to the sizes the launch was planned for.
+__device__ __forceinline__ int listed_rows(const int32_t* row_ptr, const int32_t* nb_ptr,
+                                           int nb_max, int m_max) {
+  int nb = *nb_ptr;
+  nb = nb < 0 ? 0 : (nb > nb_max ? nb_max : nb);
+  const int M = row_ptr[nb];
+  return M < 0 ? 0 : (M > m_max ? m_max : M);
+}
+
+__device__ __forceinline__ Partial shfl_xor(Partial p, int o) {
+  Partial q;
+  q.m = __shfl_xor(p.m, o, kWave);
+  q.s = __shfl_xor(p.s, o, kWave);
+  q.i = __shfl_xor(p.i, o, kWave);
+  return q;
+}
+
+}  // namespace lopa
+
+// Host-side helpers
+#define LOPA_LAUNCH_CHECK()                                   \
+  do {                                                        \
+    if (hipGetLastError() != hipSuccess) return LOPA_ERR_HIP; \
+  } while (0)
+
+int lopa_check_dims(const lopa_dims* d);   // defined in api.hip
