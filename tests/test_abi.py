@@ -79,8 +79,9 @@ def test_null_pointers_and_k_rejected():
 def test_workspace_size_and_shortfall():
     d = _dims()
     need = lopa.workspace_bytes(d)
-    # rows x vocabulary tiles x (max, sum, argmax)
+    # rows x 128-entry vocabulary tiles x (max, sum, argmax)
     assert need == 5 * 32 * ((152064 + 127) // 128) * 12
+    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * ((152064 + 127) // 128) * 12
     fake = ctypes.c_void_p(16)
     L = lopa.lib()
     args = [fake] * 8

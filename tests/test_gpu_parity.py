@@ -166,6 +166,9 @@ HEAD_CASES = [
     ("bf16-mfma-two-groups", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=700, B=64, m=64, k=15), None),
     ("bf16-plain-hidden96", dict(dtype="bf16", Hq=3, Hkv=1, d=32, V=513, B=8, m=6, k=2), None),
     ("bf16-mfma-V1", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=1, B=4, m=4, k=1), None),
+    ("bf16-stream-12tiles", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=1000, B=32, m=30, k=5), None),
+    ("bf16-stream-1row", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=3001, B=8, m=1, k=0), None),
+    ("bf16-tiled-hidden192", dict(dtype="bf16", Hq=3, Hkv=1, d=64, V=777, B=16, m=15, k=2), None),
 ]
 
 
