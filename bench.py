@@ -147,7 +147,8 @@ def main():
         lopa.lopa_branch_build(dims, cfg.k, cfg.tau, x["tok"], x["conf"], x["arg"], buf.nb,
                                buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr)
         e[1].record(stream)
-        lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H)
+        lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H,
+                              buf.ws)
         e[2].record(stream)
         lopa.lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
                               buf.arg, None, buf.ws)

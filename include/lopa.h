@@ -84,8 +84,10 @@ int lopa_abi_version(void);
 /* Static English text for a lopa_status value (never NULL). */
 const char* lopa_status_string(int status);
 
-/* Bytes of device workspace lopa_lmhead_conf needs for these dims (written to
- * *bytes).  Returns LOPA_OK or LOPA_ERR_INVALID.  Pure host computation. */
+/* Bytes of device workspace that lopa_branch_attn and lopa_lmhead_conf need
+ * for these dims (written to *bytes; the larger of the two, so one buffer
+ * serves both calls of a step when they are ordered on one stream).  Returns
+ * LOPA_OK or LOPA_ERR_INVALID.  Pure host computation. */
 int lopa_workspace_bytes(const lopa_dims* dims, size_t* bytes);
 
 /*
@@ -128,11 +130,16 @@ int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
  *     nb[1] (device)
  * Out H [nb_max][B][Hq*d], rounded once to dtype (bf16: nearest-even).
  *     Slots b >= nb are not written.
- * Accumulation and softmax in float32.
+ *     ws, ws_bytes  device workspace of at least lopa_workspace_bytes() (may
+ *                   be NULL/0 when that is 0): partials when the prefix is
+ *                   split across workgroups.
+ * Accumulation and softmax in float32 (bf16: MFMA products, the softmax
+ * weights enter the value product as a bf16 high + low pair).
  */
 int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const void* Vp,
                      const void* Qb, const void* Kb, const void* Vb,
-                     const int32_t* nb, void* H, hipStream_t stream);
+                     const int32_t* nb, void* H, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /*
  * Verify, LM head: for every listed row r = rows[m] (m < M = row_ptr[nb]),

@@ -63,7 +63,8 @@ _SIGS = {
     "lopa_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "lopa_branch_build": ([ctypes.POINTER(Dims), _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                           ctypes.c_int),
-    "lopa_branch_attn": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "lopa_branch_attn": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                         ctypes.c_int),
     "lopa_lmhead_conf": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                          ctypes.c_int),
     "lopa_branch_select": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -145,12 +146,13 @@ def lopa_branch_build(dims, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows, r
         _ptr(rows, i32, "rows"), _ptr(row_ptr, i32, "row_ptr"), _stream(stream)))
 
 
-def lopa_branch_attn(dims, Kp, Vp, Qb, Kb, Vb, nb, H, stream=None) -> None:
+def lopa_branch_attn(dims, Kp, Vp, Qb, Kb, Vb, nb, H, ws=None, stream=None) -> None:
     import torch
     a = _act_dtype(dims)
     _check("lopa_branch_attn", lib().lopa_branch_attn(
         ctypes.byref(dims), _ptr(Kp, a, "Kp"), _ptr(Vp, a, "Vp"), _ptr(Qb, a, "Qb"),
         _ptr(Kb, a, "Kb"), _ptr(Vb, a, "Vb"), _ptr(nb, torch.int32, "nb"), _ptr(H, a, "H"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
 
 

@@ -1,7 +1,7 @@
 // Library-wide entry points: version, status text, dimension checks and the
 // LM-head workspace size.  Pure host code: nothing here touches the GPU.
 #include "lopa_common.hpp"
-#include "lmhead_plan.hpp"
+#include "plan.hpp"
 
 extern "C" int lopa_abi_version(void) { return LOPA_ABI_VERSION; }
 
@@ -37,6 +37,6 @@ extern "C" int lopa_workspace_bytes(const lopa_dims* dims, size_t* bytes) {
   int st = lopa_check_dims(dims);
   if (st != LOPA_OK) return st;
   if (!bytes) return LOPA_ERR_INVALID;
-  *bytes = lopa::lmhead_workspace_bytes(*dims);
+  *bytes = lopa::workspace_bytes(*dims);
   return LOPA_OK;
 }

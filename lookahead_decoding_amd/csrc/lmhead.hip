@@ -28,7 +28,7 @@
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
 #include "lopa_common.hpp"
-#include "lmhead_plan.hpp"
+#include "plan.hpp"
 
 namespace lopa {
 

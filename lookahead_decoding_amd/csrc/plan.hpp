@@ -1,5 +1,5 @@
-// Launch plan of the LM-head call, shared by the entry point and the
-// workspace query so both always agree.
+// Launch plans of the attention and LM-head calls, shared by the entry
+// points and the workspace query so all three always agree.
 #pragma once
 
 #include <stddef.h>
@@ -51,6 +51,54 @@ inline HeadPlan head_plan(const lopa_dims& d) {
 inline size_t lmhead_workspace_bytes(const lopa_dims& d) {
   const HeadPlan p = head_plan(d);
   return static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 12u;
+}
+
+// Attention MFMA kernel (bf16, d = 128, (B * Hq/Hkv) % 16 == 0): workgroups
+// of 128 query rows per KV head; the committed prefix may be split over
+// grid.z when that is the only way to occupy the chip, with the splits'
+// unnormalised partials merged by a second kernel.
+constexpr int kAttnRowsPerWG = 128;
+constexpr int kAttnKeysPerBlock = 64;
+
+struct AttnPlan {
+  bool mfma;
+  int row_groups;  // grid.x
+  int splits;      // grid.z
+};
+
+inline AttnPlan attn_plan(const lopa_dims& d) {
+  AttnPlan p{};
+  const int G = d.Hq / d.Hkv;
+  p.mfma = d.dtype == LOPA_BF16 && d.d == 128 && (d.B * G) % 16 == 0;
+  p.splits = 1;
+  if (!p.mfma) return p;
+  const int rows = (d.k_max + 1) * d.B * G;
+  p.row_groups = (rows + kAttnRowsPerWG - 1) / kAttnRowsPerWG;
+  const int wgs = p.row_groups * d.Hkv;
+  const int blocks = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
+  // split only when one pass leaves most compute units idle and every split
+  // keeps at least 8 key blocks
+  if (wgs < 256 && blocks >= 16) {
+    int s = 256 / wgs;
+    if (s > blocks / 8) s = blocks / 8;
+    p.splits = s < 1 ? 1 : s;
+  }
+  return p;
+}
+
+// Partials of the split prefix: per split, KV head and query row, the
+// unnormalised output (d floats), the running max and the running sum.
+inline size_t attn_workspace_bytes(const lopa_dims& d) {
+  const AttnPlan p = attn_plan(d);
+  if (p.splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(d.k_max + 1) * d.B * (d.Hq / d.Hkv);
+  return static_cast<size_t>(p.splits) * d.Hkv * rows * (d.d + 2) * 4u;
+}
+
+inline size_t workspace_bytes(const lopa_dims& d) {
+  const size_t a = attn_workspace_bytes(d);
+  const size_t h = lmhead_workspace_bytes(d);
+  return a > h ? a : h;
 }
 
 }  // namespace lopa

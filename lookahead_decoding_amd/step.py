@@ -57,7 +57,7 @@ def run_step(dims: Dims, k: int, tau: float, x: dict, buf: StepBuffers, stream=N
     tensors tok, conf, arg (step-start state) and Kp, Vp, Qb, Kb, Vb, W."""
     lopa_branch_build(dims, k, tau, x["tok"], x["conf"], x["arg"], buf.nb, buf.br_tok,
                       buf.br_mask, buf.rows, buf.row_ptr, stream)
-    lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H, stream)
+    lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H, buf.ws, stream)
     lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg,
                      logits_out, buf.ws, stream)
     lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
@@ -77,7 +77,7 @@ def initial_pass(dims: Dims, tok: np.ndarray, x: dict, buf: StepBuffers, stream=
     rows[:len(masked)] = torch.from_numpy(masked).to(dev)
     row_ptr = torch.full((dims.nb_max + 1,), len(masked), dtype=torch.int32, device=dev)
     row_ptr[0] = 0
-    lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], nb1, buf.H, stream)
+    lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], nb1, buf.H, buf.ws, stream)
     conf = torch.zeros(dims.nb_max * B, dtype=torch.float32, device=dev)
     arg = torch.full((dims.nb_max * B,), -1, dtype=torch.int32, device=dev)
     lopa_lmhead_conf(dims, buf.H, x["W"], rows, row_ptr, nb1, conf, arg, None, buf.ws, stream)

@@ -70,8 +70,10 @@ def test_null_pointers_and_k_rejected():
     assert L.lopa_branch_build(ctypes.byref(d), 0, 0.9, None, *([fake] * 7), None) == -1
     assert L.lopa_branch_build(ctypes.byref(d), 5, 0.9, *([fake] * 8), None) == -1   # k > k_max
     assert L.lopa_branch_build(ctypes.byref(d), -1, 0.9, *([fake] * 8), None) == -1
-    assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None) == -1
-    assert L.lopa_branch_attn(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, None) == -1
+    assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake,
+                              1 << 30, None) == -1
+    assert L.lopa_branch_attn(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, fake,
+                              1 << 30, None) == -1
     assert L.lopa_branch_select(ctypes.byref(d), *([fake] * 9), None, None) == -1
     assert L.lopa_lmhead_conf(None, *([fake] * 8), fake, 1 << 30, None) == -1
 

@@ -135,6 +135,8 @@ ATTN_CASES = [
     ("bf16-mfma-span", dict(dtype="bf16", L=70, B=32, Hq=14, Hkv=2, d=128, k=4), 4),
     ("bf16-mfma-G1", dict(dtype="bf16", L=129, B=16, Hq=2, Hkv=2, d=128, k=3), 4),
     ("bf16-plain-d64", dict(dtype="bf16", L=33, B=8, Hq=4, Hkv=2, d=64, k=2), 3),
+    ("bf16-mfma-split3", dict(dtype="bf16", L=1500, B=16, m=8, Hq=4, Hkv=1, d=128, k=2), 3),
+    ("bf16-mfma-split-nb1", dict(dtype="bf16", L=1100, B=16, m=8, Hq=8, Hkv=2, d=128, k=3), 1),
     ("f32-gqa-d96", dict(L=1030, B=5, m=3, Hq=6, Hkv=3, d=96, k=1), 2),
 ]
 
@@ -148,7 +150,7 @@ def test_gpu_attn(name, ov, nb):
     buf = StepBuffers(dims)
     buf.H.fill_(7.0)                        # slots b >= nb must stay untouched
     lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"],
-                          to_device(np.array([nb], np.int32)), buf.H)
+                          to_device(np.array([nb], np.int32)), buf.H, buf.ws)
     torch.cuda.synchronize()
     Hg = act_to_f64(buf.H)
     Hx = O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv)
