@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the oracle's timed CPU work")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run 3 device copies of 1 GiB (a reference for byte counters)")
     return ap.parse_args()
 
 
@@ -196,6 +198,13 @@ def main():
                      "algorithmic_bytes_per_call": alg["head_bytes"],
                      "mfma_tflops": round(alg["head_flops"] / (head_us * 1e-6) / 1e12, 1)},
     }
+    if args.copy_probe:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = a.numel() * a.element_size()
     if not args.no_cpu_baseline:
         import oracle as O  # noqa: F401  (CPU baseline leg only)
         c, a, _ = O.initial_state(inp)

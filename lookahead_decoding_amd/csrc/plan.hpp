@@ -8,15 +8,17 @@
 
 namespace lopa {
 
-// MFMA kernel (bf16): 128 vocabulary rows per workgroup.  Variants by the
-// device-side row count M: small (M <= 160, 64-wide K chunks), mid
-// (161..384, 64-wide), large (> 384, 32-wide K chunks, row groups of 576).
-// Without hidden % 128 == 0 only the large variant (hidden % 64 == 0) runs,
-// for every M.
-constexpr int kHeadVocabPerWG = 128;
-constexpr int kHeadSmallRows = 160;
-constexpr int kHeadMidRows = 384;
-constexpr int kHeadGroupRows = 576;
+// MFMA kernel (bf16): kHeadParts persistent workgroups, one per compute
+// unit of an MI355X, each owning a balanced contiguous vocabulary range.
+// Variants by the device-side row count M (64-wide K chunks): small
+// (M <= 128, 256 vocabulary rows per pass), mid (129..256, 128 rows per
+// pass), large (> 256, 128 rows per pass, balanced row groups of at most
+// 320 rows, each group streaming the weight once).  hidden must be a
+// multiple of 128.
+constexpr int kHeadParts = 256;
+constexpr int kHeadSmallRows = 128;
+constexpr int kHeadMidRows = 256;
+constexpr int kHeadGroupRows = 320;
 // Plain kernel (float32, or shapes outside the MFMA kernel): one vocabulary
 // entry per thread, 256 per workgroup.
 constexpr int kPlainVocabPerWG = 256;
@@ -25,7 +27,7 @@ struct HeadPlan {
   bool small, mid, large;  // which MFMA variants are enqueued
   int large_lo;            // the large variant serves M > large_lo
   int groups;              // row groups of the large variant (grid.y)
-  int ntiles;              // vocabulary tiles = partials per row
+  int ntiles;              // vocabulary parts = partials per row
   int m_max;               // nb_max * B
 };
 
@@ -35,14 +37,12 @@ inline HeadPlan head_plan(const lopa_dims& d) {
   p.m_max = (d.k_max + 1) * d.B;
   const bool bf16 = d.dtype == LOPA_BF16;
   const bool k128 = bf16 && hidden % 128 == 0;
-  const bool k64 = bf16 && hidden % 64 == 0;
   p.small = k128;
   p.mid = k128 && p.m_max > kHeadSmallRows;
-  p.large = k64 && (!k128 || p.m_max > kHeadMidRows);
-  p.large_lo = k128 ? kHeadMidRows : 0;
+  p.large = k128 && p.m_max > kHeadMidRows;
+  p.large_lo = kHeadMidRows;
   p.groups = (p.m_max + kHeadGroupRows - 1) / kHeadGroupRows;
-  p.ntiles = k64 ? (d.V + kHeadVocabPerWG - 1) / kHeadVocabPerWG
-                 : (d.V + kPlainVocabPerWG - 1) / kPlainVocabPerWG;
+  p.ntiles = k128 ? kHeadParts : (d.V + kPlainVocabPerWG - 1) / kPlainVocabPerWG;
   return p;
 }
 

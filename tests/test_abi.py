@@ -81,9 +81,12 @@ def test_null_pointers_and_k_rejected():
 def test_workspace_size_and_shortfall():
     d = _dims()
     need = lopa.workspace_bytes(d)
-    # rows x 128-entry vocabulary tiles x (max, sum, argmax)
-    assert need == 5 * 32 * ((152064 + 127) // 128) * 12
-    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * ((152064 + 127) // 128) * 12
+    # rows x 256 vocabulary parts x (max, sum, argmax)
+    assert need == 5 * 32 * 256 * 12
+    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 12
+    # a long prefix split over workgroups: attention partials dominate
+    split = _dims(L=4096, B=64, k_max=8)
+    assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 64 * 7) * 130 * 4
     fake = ctypes.c_void_p(16)
     L = lopa.lib()
     args = [fake] * 8
