@@ -14,16 +14,15 @@
 // (max, sum exp(l - max), argmax); a merge kernel folds the parts of a row.
 //   k_lmhead_mfma   bf16.  One persistent workgroup per compute unit owns a
 //                   balanced contiguous vocabulary range and every LM-head
-//                   row of its row group.  Four producer waves fetch 64-wide
-//                   K chunks of W and H with row-contiguous 16-byte buffer
-//                   loads into a register ring several chunks deep and write
-//                   them to a double-buffered XOR-swizzled LDS tile; four
-//                   compute waves read v_mfma_f32_32x32x16_bf16 fragments
-//                   from it.  W is read from HBM exactly once.  The row count
-//                   M lives on the device: each variant is enqueued when M
-//                   could fall in its range and returns at once otherwise;
-//                   inside a variant the 32-row tile count picks a body
-//                   compiled for it.
+//                   row of its row group.  Four producer waves move 64-wide
+//                   K chunks of W and H straight from HBM/L2 into a
+//                   three-stage XOR-swizzled LDS ring with buffer loads that
+//                   write LDS; four compute waves read
+//                   v_mfma_f32_32x32x16_bf16 fragments from it.  W is read
+//                   from HBM exactly once.  The row count M lives on the
+//                   device and picks the body: all rows in one group up to
+//                   128, else groups of up to 256 rows whose workgroups
+//                   share the weight stream through L2.
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
 #include "lopa_common.hpp"
@@ -78,175 +77,179 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
 
 constexpr int kKC = 64;          // K chunk
 constexpr int kRB = kKC * 2;     // bytes of one row per chunk (8 slots of 16 B)
-constexpr int kRPP = 32;         // rows per staging load (256 producer threads / 8 slots)
+constexpr int kStages = 3;       // LDS stages: S - 1 chunks in flight while one is computed
+constexpr int kRunRows = 512;    // running partials: compute-wave columns x rows
 
-template <int NVW, int HRMAX>
-struct HeadSmem {
-  static constexpr int WROWS = 128 * NVW;                // vocabulary rows per pass
-  static constexpr int HRP = (HRMAX + kRPP - 1) / kRPP * kRPP;
-  static constexpr int BUF = (WROWS + HRP) * kRB;        // bytes per staging buffer
-  static constexpr int RUN = 4 * HRMAX * 12;             // running partials [4 waves][rows]
-  static constexpr int BYTES = 2 * BUF + RUN;
+// Shape of one body: WX x (4 / WX) compute waves over (vocabulary, rows);
+// each wave holds NVW 32-row vocabulary tiles against MTW 32-row tiles of H.
+template <int WX, int NVW, int MTW>
+struct HeadTile {
+  static constexpr int WY = 4 / WX;
+  static constexpr int WROWS = WX * NVW * 32;       // vocabulary rows per pass
+  static constexpr int HROWS = WY * MTW * 32;       // LM-head rows staged per chunk
+  static constexpr int BUF = (WROWS + HROWS) * kRB; // bytes per LDS stage
+  static constexpr int WP = WROWS / 32;             // W DMA loads per producer wave per chunk
+  static constexpr int HP = HROWS / 32;             // H DMA loads per producer wave per chunk
+  static constexpr int RUNS = kRunRows / WX;        // running-partial stride per wave column
+  static_assert(HROWS <= RUNS, "running partials");
 };
+constexpr int kHeadStage = (256 + 128) * kRB;        // largest BUF of the bodies below
+constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * 12;
 
-// One persistent workgroup per compute unit owns a contiguous, balanced
-// range of the vocabulary (a multiple of 16 rows) and every LM-head row of
-// its row group; it walks the range in passes of 128*NVW vocabulary rows and
-// each pass walks the full hidden dimension in 64-wide K chunks.
+// s_waitcnt on the vector-memory counter only (lgkm and exp counts left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+#define LOPA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One persistent workgroup owns a contiguous, balanced vocabulary range
+// (multiples of 16 rows) of its part and the Mg rows of its row group; it
+// walks the range in passes of WROWS vocabulary rows, each pass the full
+// hidden dimension in 64-wide K chunks.
 //
-// The workgroup is warp-specialised (512 threads).  Waves 4..7 only move
-// data: they fetch each chunk of W and of H with row-contiguous 16-byte
-// buffer loads (8 threads per 128-byte row segment) into a register ring D
-// chunks deep -- so D-1 chunks (tens of KB per compute unit) stay in flight
-// -- and write it to a double-buffered, XOR-swizzled LDS tile.  Waves 0..3
-// only compute: each takes NVW 32-row tiles of W against every 32-row tile
-// of H with v_mfma_f32_32x32x16_bf16 straight from LDS.  One barrier per
-// chunk.  After each pass the compute waves fold their logits into a running
-// (max, sum, argmax) per row in LDS; at the end the four are merged and one
-// partial per row is written.  W is addressed through a buffer descriptor
-// covering exactly the workgroup's range: loads past it return zeros
-// without touching memory, so a ragged range needs no clamping.
-template <int NVW, int MT, int HRMAX, int D>
-__device__ __forceinline__ void head_body(int V, int hidden, int nparts, int Mg, int row0,
-                                          int h_bytes, const unsigned short* __restrict__ H,
+// Warp-specialised, 512 threads.  Waves 4..7 only issue loads: each 128-byte
+// row segment of a chunk is fetched by 8 lanes with 16-byte buffer loads
+// that write straight into LDS (no registers on the way), 8 rows per
+// instruction, in the XOR-swizzled order the fragment reads expect.  Three
+// LDS stages: while the compute waves work on chunk i, chunks i+1 and i+2 are
+// in flight; the producers issue chunk i+2 once the barrier that ends chunk
+// i-1 shows its stage is free, and wait for chunk i+1 to land before the
+// next barrier.  Waves 0..3 only compute: v_mfma_f32_32x32x16_bf16 with the
+// A operand from W and the B operand from H, fragments read from LDS.  After
+// each pass a wave folds its logits into a running (max, sum, argmax) per
+// row in LDS; at the end the wave columns are merged and one partial per row
+// is written.  W is addressed through a buffer descriptor covering exactly
+// the workgroup's range, so loads past it return zeros without touching
+// memory.  Chunks are visited in an order rotated by the part, so the
+// compute units of one XCD do not all ask for the same H lines at once.
+template <int WX, int NVW, int MTW, int W_AUX>
+__device__ __forceinline__ void head_body(int V, int hidden, int nparts, int part, int Mg,
+                                          int row0, int h_bytes,
+                                          const unsigned short* __restrict__ H,
                                           const unsigned short* __restrict__ W,
-                                          const int32_t* __restrict__ rows,
-                                          unsigned char* smem, float* __restrict__ ws_m,
-                                          float* __restrict__ ws_s, int32_t* __restrict__ ws_i,
+                                          const int32_t* __restrict__ rows, unsigned char* smem,
+                                          float* __restrict__ ws_m, float* __restrict__ ws_s,
+                                          int32_t* __restrict__ ws_i,
                                           float* __restrict__ logits_out) {
-  using SM = HeadSmem<NVW, HRMAX>;
-  constexpr int BUF = SM::BUF, WROWS = SM::WROWS;
-  constexpr int WP = WROWS / kRPP;                 // W loads per producer thread per chunk
-  constexpr int HP = (MT * 32 + kRPP - 1) / kRPP;  // H loads per producer thread per chunk
-  constexpr int NS = WP + HP;
-  constexpr int KS = kKC / 16;                     // MFMA K steps per chunk
+  using T = HeadTile<WX, NVW, MTW>;
+  constexpr int WROWS = T::WROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
+  constexpr int KS = kKC / 16;   // MFMA K steps per chunk
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int row_bytes = hidden * 2;
 
-  // this workgroup's vocabulary range [v_lo, v_hi)
   const int t16 = (V + 15) >> 4;
-  const int part = blockIdx.x;
   const int v_lo = static_cast<int>(static_cast<long long>(part) * t16 / nparts) * 16;
   const int v_hi = min(static_cast<int>(static_cast<long long>(part + 1) * t16 / nparts) * 16, V);
   const int npass = (v_hi - v_lo + WROWS - 1) / WROWS;
   const int nch = hidden / kKC;
   const int total = npass * nch;
+  const int rot = ((part >> 3) * nch / 32) % nch;
 
-  Partial* run = reinterpret_cast<Partial*>(smem + 2 * BUF);   // [4][HRMAX]
-  for (int r = tid; r < 4 * HRMAX; r += 512) run[r] = empty_partial();
+  Partial* run = reinterpret_cast<Partial*>(smem + kStages * kHeadStage);
+  for (int r = tid; r < kRunRows; r += 512) run[r] = empty_partial();
+  __syncthreads();
 
   if (w >= 4) {
     // ---------------- producer waves ----------------
-    const int ptid = tid - 256;
-    const int slot = ptid & 7;
-    const int rin = ptid >> 3;
+    const int pw = w - 4;
+    const int r8 = lane >> 3;                    // row within an 8-row load
+    const int ls = (lane & 7) ^ r8 ^ (pw & 1);   // logical slot landing in physical slot lane & 7
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned short*>(W) + static_cast<size_t>(v_lo) * hidden, 0,
         max(v_hi - v_lo, 0) * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t hr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
-    const int wvoff = rin * row_bytes + slot * 16;
-    int hvoff[HP];
+    // load p of this wave covers rows 8 * (4p + pw) .. +8 of the chunk
+    const int wv = (8 * pw + r8) * row_bytes + ls * 16;
+    int hv[HP];
 #pragma unroll
     for (int p = 0; p < HP; ++p)
-      hvoff[p] = rows[row0 + min(p * kRPP + rin, Mg - 1)] * row_bytes + slot * 16;
-    // swz(r + 32, s) == swz(r, s): every load of a thread uses the same slot
-    const int dst0 = rin * kRB + swz<kKC>(rin, slot) * 16;
-    u16x8 ring[D][NS];
-    // chunk i = pass * nch + k-chunk, clamped to the last one
-    auto load = [&](int i, u16x8 (&st)[NS]) {
+      hv[p] = rows[row0 + min(8 * (4 * p + pw) + r8, Mg - 1)] * row_bytes + ls * 16;
+    // chunk i -> stage i % kStages; past the end the last chunk is loaded
+    // again into the free stage so every iteration issues the same count
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      unsigned char* dst = smem + (i % kStages) * BUF;
       i = min(i, total - 1);
-      const int k = (i % nch) * kRB;
-      const int wbase = (i / nch) * WROWS * row_bytes + k;
+      const int pass = i / nch;
+      int kc = i - pass * nch + rot;
+      kc = kc >= nch ? kc - nch : kc;
+      const int sw = pass * WROWS * row_bytes + kc * kRB;
 #pragma unroll
       for (int p = 0; p < WP; ++p)
-        st[p] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              wr, wvoff, wbase + p * kRPP * row_bytes, 2));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + pw) * 1024), 16, wv,
+                                                 sw + 32 * p * row_bytes, 0, W_AUX);
 #pragma unroll
       for (int p = 0; p < HP; ++p)
-        st[WP + p] = __builtin_bit_cast(
-            u16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, hvoff[p], k, 0));
-    };
-    auto store = [&](int b, const u16x8 (&st)[NS]) {
-      unsigned char* base = smem + b * BUF + dst0;
-#pragma unroll
-      for (int p = 0; p < WP; ++p) *reinterpret_cast<u16x8*>(base + p * kRPP * kRB) = st[p];
-#pragma unroll
-      for (int p = 0; p < HP; ++p)
-        *reinterpret_cast<u16x8*>(base + (WROWS + p * kRPP) * kRB) = st[WP + p];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            hr, LOPA_LDS(dst + WROWS * kRB + (4 * p + pw) * 1024), 16, hv[p], kc * kRB, 0, 0);
     };
     if (total > 0) {
 #pragma unroll
-      for (int u = 0; u < D; ++u) load(u, ring[u]);
-      store(0, ring[0]);
-      load(D, ring[0]);
-    }
-    __syncthreads();
-    // iteration i: the compute waves read buffer i%2; here chunk i+1 goes to
-    // buffer (i+1)%2 and its ring slot is refilled with chunk i+1+D
-    // full groups of 2*D iterations without conditions (so the compiler's
-    // wait counts stay exact and D-1 chunks remain in flight), then a tail
-    int i0 = 0;
-    for (; i0 + 2 * D <= total; i0 += 2 * D) {
-#pragma unroll
-      for (int u = 0; u < 2 * D; ++u) {
-        store((u + 1) & 1, ring[(u + 1) % D]);
-        load(i0 + u + 1 + D, ring[(u + 1) % D]);
-        __syncthreads();
+      for (int u = 0; u < kStages - 1; ++u) issue(u);
+      wait_vmcnt<(kStages - 2) * (WP + HP)>();
+      __builtin_amdgcn_s_barrier();
+      for (int i = 0; i + 1 < total; ++i) {
+        issue(i + kStages - 1);
+        wait_vmcnt<(kStages - 2) * (WP + HP)>();
+        __builtin_amdgcn_s_barrier();
       }
     }
-#pragma unroll
-    for (int u = 0; u < 2 * D; ++u) {
-      if (i0 + u < total) {
-        store((u + 1) & 1, ring[(u + 1) % D]);
-        load(i0 + u + 1 + D, ring[(u + 1) % D]);
-      }
-      if (i0 < total) __syncthreads();
-    }
+    wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
   } else {
     // ---------------- compute waves ----------------
+    const int wx = w % WX;
+    const int wy = w / WX;
     const int ln = lane & 31;     // MFMA row / column within a 32-tile
     const int lh = lane >> 5;     // which 8 of the 16 K values of a step
-    f32x16 acc[MT][NVW];
+    f32x16 acc[MTW][NVW];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
-    auto compute = [&](int b) {
+    auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NVW], u16x8 (&hf)[MTW])
+        __attribute__((always_inline)) {
+      const int s = j * 2 + lh;   // logical slot: K values 16j + 8lh .. +8
+#pragma unroll
+      for (int n = 0; n < NVW; ++n) {
+        const int r = (wx * NVW + n) * 32 + ln;
+        wf[n] = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        const int r = (wy * MTW + mt) * 32 + ln;
+        hf[mt] = *reinterpret_cast<const u16x8*>(base + (WROWS + r) * kRB + swz<kKC>(r, s) * 16);
+      }
+    };
+    auto compute = [&](int b) __attribute__((always_inline)) {
       const unsigned char* base = smem + b * BUF;
+      u16x8 wf[2][NVW], hf[2][MTW];
+      frags(base, 0, wf[0], hf[0]);
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        const int ls = j * 2 + lh;   // logical slot: K values 16j + 8lh .. +8
-        u16x8 wf[NVW];
+        if (j + 1 < KS) frags(base, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
 #pragma unroll
-        for (int n = 0; n < NVW; ++n) {
-          const int r = w * (32 * NVW) + n * 32 + ln;
-          wf[n] = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, ls) * 16);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int r = mt * 32 + ln;
-          const u16x8 hf =
-              *reinterpret_cast<const u16x8*>(base + (WROWS + r) * kRB + swz<kKC>(r, ls) * 16);
+        for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
           for (int n = 0; n < NVW; ++n)
             acc[mt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, wf[n]), __builtin_bit_cast(bf16x8, hf), acc[mt][n],
-                0, 0, 0);
-        }
+                __builtin_bit_cast(bf16x8, wf[j & 1][n]), __builtin_bit_cast(bf16x8, hf[j & 1][mt]),
+                acc[mt][n], 0, 0, 0);
       }
     };
-    // acc[mt][n][r] = logit of row 32mt + ln, vocabulary entry
-    // vbw + 32n + 8(r/4) + 4lh + r%4
+    // acc[mt][n][q] = logit of row (wy*MTW + mt)*32 + ln, vocabulary entry
+    // vbw + 32n + 8(q/4) + 4lh + q%4
     auto finish_pass = [&](int pass) {
-      const int vbw = v_lo + pass * WROWS + w * (32 * NVW);
+      const int vbw = v_lo + pass * WROWS + wx * (32 * NVW);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MTW; ++mt) {
         const Partial p = row_partial<NVW>(acc[mt], vbw, lh, v_hi);
-        const int r = mt * 32 + ln;
-        if (lh == 0) run[w * HRMAX + r] = merge(run[w * HRMAX + r], p);
+        const int r = (wy * MTW + mt) * 32 + ln;
+        if (lh == 0) run[wx * T::RUNS + r] = merge(run[wx * T::RUNS + r], p);
         if (logits_out && r < Mg) {
           const size_t lb = static_cast<size_t>(rows[row0 + r]) * V;
 #pragma unroll
@@ -261,31 +264,17 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int Mg,
         for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
       }
     };
-    __syncthreads();
-    int i0 = 0;
-    for (; i0 + 2 * D <= total; i0 += 2 * D) {
-#pragma unroll
-      for (int u = 0; u < 2 * D; ++u) {
-        compute(u & 1);
-        if ((i0 + u) % nch == nch - 1) finish_pass((i0 + u) / nch);
-        __syncthreads();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2 * D; ++u) {
-      if (i0 + u < total) {
-        compute(u & 1);
-        if ((i0 + u) % nch == nch - 1) finish_pass((i0 + u) / nch);
-      }
-      if (i0 < total) __syncthreads();
+    for (int i = 0; i < total; ++i) {
+      __syncthreads();
+      compute(i % kStages);
+      if (i % nch == nch - 1) finish_pass(i / nch);
     }
   }
   __syncthreads();
   for (int r = tid; r < Mg; r += 512) {
     Partial p = run[r];
-    p = merge(p, run[HRMAX + r]);
-    p = merge(p, run[2 * HRMAX + r]);
-    p = merge(p, run[3 * HRMAX + r]);
+#pragma unroll
+    for (int x = 1; x < WX; ++x) p = merge(p, run[x * T::RUNS + r]);
     const size_t o = static_cast<size_t>(row0 + r) * nparts + part;
     ws_m[o] = p.m;
     ws_s[o] = p.s;
@@ -293,42 +282,43 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int Mg,
   }
 }
 
-// Variant serving total row counts M in (m_lo, m_hi]: balanced row groups of
-// at most 32*MTHI rows (grid.y); the group's 32-row tile count picks a body
-// compiled for exactly that many tiles.
-template <int NVW, int MTLO, int MTHI, int D>
+// kHeadParts workgroups of 512 threads, one per compute unit.  Block b sits
+// on XCD b % 8; the row groups of one vocabulary part take consecutive
+// blocks of the same XCD, so they stream the same weight lines together and
+// the second reader is served from that XCD's L2 (or the MALL behind it).
 __global__ void __launch_bounds__(512)
-k_lmhead_mfma(int V, int hidden, int nparts, int nb_max, int m_max, int m_lo, int m_hi,
-              int h_bytes, const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
+k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
+              const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
               float* __restrict__ ws_s, int32_t* __restrict__ ws_i,
               float* __restrict__ logits_out) {
-  constexpr int HRMAX = MTHI * 32;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[HeadSmem<NVW, HRMAX>::BYTES];
-  const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
-  if (M <= m_lo || M > m_hi) return;
-  // balanced row groups of at most MTHI tiles
-  const int mt_all = (M + 31) >> 5;
-  const int ngroups = (mt_all + MTHI - 1) / MTHI;
-  const int tpg = (mt_all + ngroups - 1) / ngroups;
-  const int row0 = blockIdx.y * tpg * 32;
-  if (static_cast<int>(blockIdx.y) >= ngroups || row0 >= M) return;
-  const int Mg = min(M - row0, tpg * 32);
-  int Mt = (Mg + 31) >> 5;
-  Mt = Mt < MTLO ? MTLO : Mt;
-  switch (Mt) {
-#define LOPA_BODY(T)                                                                           \
-  case T:                                                                                      \
-    if constexpr (T >= MTLO && T <= MTHI)                                                      \
-      head_body<NVW, T, HRMAX, D>(V, hidden, nparts, Mg, row0, h_bytes, H, W, rows, smem,     \
-                                  ws_m, ws_s, ws_i, logits_out);                               \
-    break;
-    LOPA_BODY(1) LOPA_BODY(2) LOPA_BODY(3) LOPA_BODY(4) LOPA_BODY(5) LOPA_BODY(6)
-    LOPA_BODY(7) LOPA_BODY(8) LOPA_BODY(9) LOPA_BODY(10)
-#undef LOPA_BODY
-    default: break;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kHeadSmem];
+  const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
+  if (M <= 0) return;
+  const HeadGroups g = head_groups(M);
+  const int b = blockIdx.x;
+  const int q = b >> 3;
+  const int group = q % g.groups;
+  const int part = (q / g.groups) * 8 + (b & 7);
+  const int row0 = group * g.tpg * 32;
+  if (part >= g.nparts || row0 >= M) return;
+  const int Mg = min(M - row0, g.tpg * 32);
+#define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
+                  logits_out
+  if (!g.wide) {
+    switch (g.tpg) {
+      case 1: head_body<4, 2, 1, 2>(LOPA_ARGS); break;
+      case 2: head_body<4, 2, 2, 2>(LOPA_ARGS); break;
+      case 3: head_body<4, 2, 3, 2>(LOPA_ARGS); break;
+      default: head_body<4, 2, 4, 2>(LOPA_ARGS); break;
+    }
+  } else if (g.tpg <= 6) {
+    head_body<2, 2, 3, 0>(LOPA_ARGS);
+  } else {
+    head_body<2, 2, 4, 0>(LOPA_ARGS);
   }
+#undef LOPA_ARGS
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +366,7 @@ k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256)
-k_lmhead_merge(int ntiles, int nb_max, int m_max,
+k_lmhead_merge(int ntiles, int mfma, int nb_max, int m_max,
                const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
                const int32_t* __restrict__ nb_ptr, const float* __restrict__ ws_m,
                const float* __restrict__ ws_s, const int32_t* __restrict__ ws_i,
@@ -385,6 +375,7 @@ k_lmhead_merge(int ntiles, int nb_max, int m_max,
   const int m = blockIdx.x;
   const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
   if (m >= M) return;
+  if (mfma) ntiles = head_groups(M).nparts;
   Partial p = empty_partial();
   const size_t base = static_cast<size_t>(m) * ntiles;
   for (int t = threadIdx.x; t < ntiles; t += 256)
@@ -425,25 +416,10 @@ extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void
   const unsigned short* Hb = static_cast<const unsigned short*>(H);
   const unsigned short* Wb = static_cast<const unsigned short*>(W);
   const int h_bytes = p.m_max * hidden * 2;   // H is [nb_max][B][hidden]
-  if (p.small) {
-    hipLaunchKernelGGL((k_lmhead_mfma<2, 1, 4, 4>), dim3(p.ntiles), dim3(512), 0, stream, V,
-                       hidden, p.ntiles, nb_max, p.m_max, 0, kHeadSmallRows, h_bytes, Hb, Wb, rows,
-                       row_ptr, nb, wm, wsum, wi, logits_out);
-    LOPA_LAUNCH_CHECK();
-  }
-  if (p.mid) {
-    hipLaunchKernelGGL((k_lmhead_mfma<1, 5, 8, 3>), dim3(p.ntiles), dim3(512), 0, stream, V,
-                       hidden, p.ntiles, nb_max, p.m_max, kHeadSmallRows, kHeadMidRows, h_bytes, Hb, Wb,
-                       rows, row_ptr, nb, wm, wsum, wi, logits_out);
-    LOPA_LAUNCH_CHECK();
-  }
-  if (p.large) {
-    hipLaunchKernelGGL((k_lmhead_mfma<1, 1, 10, 3>), dim3(p.ntiles, p.groups), dim3(512), 0,
-                       stream, V, hidden, p.ntiles, nb_max, p.m_max, p.large_lo, 1 << 30, h_bytes, Hb, Wb,
-                       rows, row_ptr, nb, wm, wsum, wi, logits_out);
-    LOPA_LAUNCH_CHECK();
-  }
-  if (!p.small && !p.mid && !p.large) {
+  if (p.mfma) {
+    hipLaunchKernelGGL(k_lmhead_mfma, dim3(kHeadParts), dim3(512), 0, stream, V, hidden, nb_max,
+                       p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi, logits_out);
+  } else {
     const dim3 grid(p.ntiles, p.m_max);
     if (dims->dtype == LOPA_F32) {
       hipLaunchKernelGGL(k_lmhead_plain<float>, grid, dim3(256), 0, stream, V, hidden, p.ntiles,
@@ -455,10 +431,10 @@ extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void
                          p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi,
                          logits_out);
     }
-    LOPA_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_lmhead_merge, dim3(p.m_max), dim3(256), 0, stream, p.ntiles, nb_max,
-                     p.m_max, rows,
+  LOPA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_lmhead_merge, dim3(p.m_max), dim3(256), 0, stream, p.ntiles,
+                     p.mfma ? 1 : 0, nb_max, p.m_max, rows,
                      row_ptr, nb, wm, wsum, wi, conf, arg);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;
