@@ -15,6 +15,7 @@ host.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +29,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+# HBM bytes per lopa_lmhead_conf call (k_lmhead_mfma + k_lmhead_merge) from two
+# rocprofv3 --pmc runs of this script: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB
+# per dispatch; the factors are what the same counters read for a 1 GiB device
+# copy).  Keyed by workload and by a hash of the kernel sources the counters
+# were taken on: after any change to those sources the figure is not reported.
+HEAD_SOURCES = ("lmhead.hip", "plan.hpp", "lopa_common.hpp")
+HEAD_TRAFFIC = {
+    "7b-bf16-L512-B32-m24-k4": ("bf02adfa5d9e91c2", 1100589632),
+}
+
+
+def head_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in HEAD_SOURCES:
+        with open(os.path.join(ROOT, "lookahead_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -130,15 +149,33 @@ def main():
             step()
         torch.cuda.synchronize()
 
+    # eager: HIP events around the LM-head call inside the timed loop itself
+    head_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+
+    def timed_step(i):
+        lopa.lopa_branch_build(dims, cfg.k, cfg.tau, x["tok"], x["conf"], x["arg"], buf.nb,
+                               buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr)
+        lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H,
+                              buf.ws)
+        head_ev[i][0].record(stream)
+        lopa.lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
+                              buf.arg, None, buf.ws)
+        head_ev[i][1].record(stream)
+        lopa.lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg,
+                                buf.bconf, buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
+
     for _ in range(args.warmup):
         graph.replay() if graph else step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay() if graph else step()
+    for i in range(args.steps):
+        graph.replay() if graph else timed_step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
+    head_timed_us = None if graph else \
+        float(np.mean([a.elapsed_time(b) for a, b in head_ev])) * 1e3
 
     # Per-call durations with HIP events on the stream the calls run on.
     K = max(20, min(args.steps, 100))
@@ -161,7 +198,11 @@ def main():
     torch.cuda.synchronize()
     per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
     call_us = per.mean(axis=0) * 1e3
-    head_us = float(call_us[2])
+    # the roofline uses the LM-head call timed inside the timed loop (eager), else the
+    # separate per-call loop (graph replay has no per-call events)
+    head_us = head_timed_us if head_timed_us is not None else float(call_us[2])
+    tr = HEAD_TRAFFIC.get(cfg.name)
+    traffic = tr[1] if tr is not None and tr[0] == head_source_hash() else None
     achieved = alg["head_bytes"] / (head_us * 1e-6) / 1e9
 
     steps_s = 1e3 / ms
@@ -194,8 +235,9 @@ def main():
         "roofline": {"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
                      "algorithmic_bytes_per_call": alg["head_bytes"],
+                     "call_us": round(head_us, 2),
                      "mfma_tflops": round(alg["head_flops"] / (head_us * 1e-6) / 1e12, 1)},
     }
     if args.copy_probe:
