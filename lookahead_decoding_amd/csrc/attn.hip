@@ -10,15 +10,18 @@
 // stored: a query row's branch follows from its index, and the kernel only
 // ever visits the prefix keys and that branch's block keys.
 //
-//   k_attn_mfma   bf16, d = 128, (B * Hq/Hkv) % 16 == 0.  A workgroup (4
-//                 waves) takes 64 query rows of one KV head -- rows are
-//                 (branch, position, q-head of the group), so the 64 rows span
-//                 several positions and at most a few branches -- and streams
-//                 the prefix K/V of that head through LDS once for all of
-//                 them.  S^T = K Q^T and O^T = V^T P^T are
-//                 v_mfma_f32_16x16x32_bf16 tiles; online softmax in float32;
-//                 P enters the PV product as a bf16 hi + lo pair so the
-//                 probabilities keep ~16 significant bits.
+//   k_attn_dma    bf16, d = 128.  A workgroup takes 128 query rows of one KV
+//                 head -- rows are (branch, position, q-head of the group), so
+//                 they span several positions and at most a few branches --
+//                 and walks 64-key work units: the committed prefix, then the
+//                 own block of each branch its rows belong to.  Four producer
+//                 waves move K and V rows into a three-stage LDS ring with
+//                 buffer-to-LDS loads; four compute waves take 32 rows each:
+//                 S^T = K Q^T and O^T = V^T P^T as v_mfma_f32_32x32x16_bf16
+//                 (V^T through transposing LDS reads), online softmax in
+//                 float32, P entering PV as a bf16 hi + lo pair so the
+//                 probabilities keep ~16 significant bits.  Units may be split
+//                 over workgroups; k_attn_combine merges the splits.
 //   k_attn_plain  any dtype / d <= 256: one wave per query row, keys in
 //                 chunks of 1024 with online softmax, float32 throughout.
 #include <type_traits>
@@ -33,303 +36,291 @@ namespace lopa {
 // ---------------------------------------------------------------------------
 
 constexpr int kAD = 128;          // head dim
-constexpr int kAKB = 64;          // keys per LDS block
-constexpr int kAKRow = kAD + 8;   // K row in LDS (bf16): 272 B, conflict-free 16-B reads
-constexpr int kAVRow = kAKB + 8;  // V^T row in LDS (bf16): 144 B, conflict-free 16-B reads
-constexpr int kARows = 128;       // query rows per workgroup (4 waves x 2 groups of 16)
+constexpr int kARows = 128;       // query rows per workgroup (4 compute waves x 32)
+// ---------------------------------------------------------------------------
+// MFMA path with buffer-to-LDS staging
+// ---------------------------------------------------------------------------
 
-// K is staged so that the QK^T tile t, MFMA row i reads key
-// 32(t/2) + 8(i/4) + 4(t%2) + i%4: the S^T accumulator of lane (i, g) then
-// holds, for the two tiles of a 32-key PV step, 8 consecutive keys
-// 32s + 8g .. 32s + 8g + 7 -- exactly the contraction slice the P^T operand
-// of that lane needs, so V^T fragments are single contiguous 16-byte reads.
-__device__ __forceinline__ int key_slot(int k) {
-  return (k & 32) | ((k & 4) << 2) | ((k & 24) >> 1) | (k & 3);
+constexpr int kAUnitKeys = 64;                 // keys per work unit
+constexpr int kARowBytes = kAD * 2;            // one key row of K or V in LDS: 256 B
+constexpr int kAHalf = kAUnitKeys * kARowBytes;  // K (or V) part of a stage: 16 KB
+constexpr int kAStages = 3;
+constexpr int kADmaPerUnit = 8;                // 16-byte LDS loads per producer wave per unit
+
+// XOR of the 16-byte slot of key row r in LDS: conflict-free for the K
+// fragment reads (16 rows, one slot) and the transposed V reads (4 rows x 32 B).
+__device__ __forceinline__ int aswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Key row read by MFMA row i of a 32-key S^T tile: with this order the 16
+// scores lane (j, h) holds are keys 16(r/8) + 8h + r%8, r = 0..15 -- the two
+// 8-key slices of P^T that lane feeds to the two 16-key PV steps of the tile.
+__device__ __forceinline__ int kperm(int i) {
+  const int a = i >> 3, h = (i >> 2) & 1, c = i & 3;
+  return ((a >> 1) << 4) | (h << 3) | ((a & 1) << 2) | c;
 }
 
-struct AttnStage {
-  u16x8 k[4];   // 4 keys' 16-byte segments
-  u16x8 v[4];   // 4 consecutive keys x 8 dims
-};
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+#define LOPA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // One workgroup: 128 query rows (branch, position, q-head of the group) of
-// KV head g, split s of the prefix keys.  Each wave owns two 16-row groups.
-// Prefix blocks are double-buffered in LDS (next block's loads in flight
-// during the current block's MFMAs); the last split also visits every
-// branch's own block, each seen only by that branch's rows.  With one split
-// the output is normalised and rounded to bf16 here; otherwise the
-// unnormalised partial (O, max, sum) goes to `part` for k_attn_combine.
-__global__ void __launch_bounds__(256)
-k_attn_mfma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
-            const int32_t* __restrict__ nb_ptr, const unsigned short* __restrict__ Kp,
-            const unsigned short* __restrict__ Vp, const unsigned short* __restrict__ Qb,
-            const unsigned short* __restrict__ Kb, const unsigned short* __restrict__ Vb,
-            unsigned short* __restrict__ H, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) unsigned short Ks[2][kAKB * kAKRow];
-  __shared__ __attribute__((aligned(16))) unsigned short Vt[2][kAD * kAVRow];
-
+// KV head g, and the work units [u_lo, u_hi) of its split -- units are the
+// 64-key blocks of the committed prefix followed by the own blocks of every
+// branch its rows belong to (a row only scores its own branch's block).
+// Waves 4..7 move K and V rows of a unit straight into an XOR-swizzled
+// three-stage LDS ring with buffer-to-LDS loads; waves 0..3 each own 32
+// query rows: S^T = K Q^T and O^T = V^T P^T as v_mfma_f32_32x32x16_bf16,
+// K fragments read in the kperm order, V^T fragments with transposing LDS
+// reads, online softmax in float32, P entering PV as a bf16 hi + lo pair.
+__global__ void __launch_bounds__(512)
+k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
+           const int32_t* __restrict__ nb_ptr, const unsigned short* __restrict__ Kp,
+           const unsigned short* __restrict__ Vp, const unsigned short* __restrict__ Qb,
+           const unsigned short* __restrict__ Kb, const unsigned short* __restrict__ Vb,
+           unsigned short* __restrict__ H, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kAStages * 2 * kAHalf];
   const int G = Hq / Hkv;
   const int g = blockIdx.y;
   const int split = blockIdx.z;
-  const int RB = B * G;                 // query rows per branch for this KV head
-  const int nb = min(max(*nb_ptr, 0), nb_max);
+  const int RB = B * G;
+  const int nb = __builtin_amdgcn_readfirstlane(min(max(*nb_ptr, 0), nb_max));
   const int R = nb * RB;
   const int r0 = blockIdx.x * kARows;
   if (r0 >= R) return;
   const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int ln = lane & 15;
-  const int lg = lane >> 4;
 
-  // two 16-row groups per wave; rows of a group share one branch
-  int grow[2], gbr[2], qoff[2];
-  bool act[2];
+  // work units of this workgroup
+  const int nbp = (L + kAUnitKeys - 1) / kAUnitKeys;
+  const int obp = (B + kAUnitKeys - 1) / kAUnitKeys;
+  const int b_lo = r0 / RB;
+  const int b_hi = (min(r0 + kARows, R) - 1) / RB;
+  const int units = nbp + (b_hi - b_lo + 1) * obp;
+  const int u_lo = static_cast<int>(static_cast<long long>(split) * units / splits);
+  const int u_hi = static_cast<int>(static_cast<long long>(split + 1) * units / splits);
+  const int n = u_hi - u_lo;
+
+  if (w >= 4) {
+    // ---------------- producer waves ----------------
+    const int pw = w - 4;
+    const int kq = lane >> 4;                    // key within a 4-key load
+    const int ps = lane & 15;                    // physical 16-byte slot
+    const __amdgpu_buffer_rsrc_t kpr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(Kp), 0, L * Hkv * kARowBytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vpr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(Vp), 0, L * Hkv * kARowBytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kbr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(Kb), 0, nb_max * B * Hkv * kARowBytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vbr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(Vb), 0, nb_max * B * Hkv * kARowBytes, 0x00020000);
+    // unit number i of this workgroup -> stage i % kAStages; past the end the
+    // last unit is loaded again into the free stage so every iteration issues
+    // the same number of loads
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      unsigned char* st = smem + (i % kAStages) * 2 * kAHalf;
+      const int u = u_lo + min(i, n - 1);
+      const bool own = u >= nbp;
+      const int v = u - nbp;
+      const int kn = own ? min(kAUnitKeys, B - (v % obp) * kAUnitKeys)
+                         : min(kAUnitKeys, L - u * kAUnitKeys);
+      const int key0 = own ? (b_lo + v / obp) * B + (v % obp) * kAUnitKeys : u * kAUnitKeys;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    // wave-uniform: keep it in scalar registers so branches on it are scalar
-    grow[q] = __builtin_amdgcn_readfirstlane(r0 + 32 * w + 16 * q);
-    act[q] = grow[q] < R;
-    gbr[q] = act[q] ? grow[q] / RB : -1;
-    qoff[q] = 0;
-    if (act[q]) {
-      const int rem = grow[q] + ln - gbr[q] * RB;
-      qoff[q] = ((gbr[q] * B + rem / G) * Hq + g * G + rem % G) * kAD;
+      for (int p = 0; p < 4; ++p) {
+        const int kr = 4 * (pw + 4 * p) + kq;    // key row of the unit
+        const int key = key0 + min(kr, kn - 1);
+        const int off = ((key * Hkv + g) * kAD + ((ps ^ aswz(kr)) << 3)) * 2;
+        unsigned char* dk = st + (pw + 4 * p) * 1024;
+        if (own) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kbr, LOPA_LDS_PTR(dk), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vbr, LOPA_LDS_PTR(dk + kAHalf), 16, off, 0, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kpr, LOPA_LDS_PTR(dk), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vpr, LOPA_LDS_PTR(dk + kAHalf), 16, off, 0, 0, 0);
+        }
+      }
+    };
+    if (n > 0) {
+#pragma unroll
+      for (int u = 0; u < kAStages - 1; ++u) issue(u);
+      attn_wait_vmcnt<(kAStages - 2) * kADmaPerUnit>();
+      __builtin_amdgcn_s_barrier();
+      for (int i = 0; i + 1 < n; ++i) {
+        issue(i + kAStages - 1);
+        attn_wait_vmcnt<(kAStages - 2) * kADmaPerUnit>();
+        __builtin_amdgcn_s_barrier();
+      }
     }
+    attn_wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+    return;
   }
-  u16x8 qf[2][4];
+
+  // ---------------- compute waves ----------------
+  const int ln = lane & 31;     // this lane's query row within the wave's 32
+  const int lh = lane >> 5;
+  const int grow = r0 + 32 * w + ln;
+  const bool row_ok = grow < R;
+  const int row = min(grow, R - 1);
+  const int rbr = row / RB;                    // branch of the row
+  const int rem = row - rbr * RB;
+  const int qoff = ((rbr * B + rem / G) * Hq + g * G + rem % G) * kAD;
+  // Q^T as the B operand: lane (j, h) holds Q[row j][16s + 8h .. +8]
+  u16x8 qf[8];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qf[q][s] = act[q] ? *reinterpret_cast<const u16x8*>(Qb + qoff[q] + 32 * s + 8 * lg)
-                        : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const u16x8*>(Qb + qoff + 16 * s + 8 * lh);
 
   const float scale2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 o[2][8];
+  float m_ref = -INFINITY;   // exponent reference of the row, log2 units
+  float l_run = 0.f;
+  f32x16 o[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) o[q][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 4; ++u) o[u] = f32x16{};
 
-  // ---- staging: kn (<= 64) keys of KV head g from key-major sources ----
-  const int kseg = tid & 15;            // K: 16-byte segment of a key row
-  const int kq = tid & 15;              // V: keys 4kq .. 4kq+3
-  const int dq = tid >> 4;              // V: dims 8dq .. 8dq+7
-  auto load_stage = [&](const unsigned short* ks, const unsigned short* vs, int kn,
-                        AttnStage& st) {
-    // keys past kn repeat key kn-1: their scores are masked to -inf, so
-    // they weigh 0 in the value product
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = min((tid >> 4) + 16 * p, kn - 1);
-      st.k[p] = *reinterpret_cast<const u16x8*>(
-          ks + (static_cast<size_t>(key) * Hkv + g) * kAD + kseg * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(4 * kq + i, kn - 1);
-      st.v[i] = *reinterpret_cast<const u16x8*>(
-          vs + (static_cast<size_t>(key) * Hkv + g) * kAD + dq * 8);
-    }
-  };
-  auto store_stage = [&](int b, const AttnStage& st) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = (tid >> 4) + 16 * p;
-      *reinterpret_cast<u16x8*>(&Ks[b][key_slot(key) * kAKRow + kseg * 8]) = st.k[p];
-    }
-    // 4 keys x 8 dims -> 8 dims x 4 consecutive keys
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const unsigned lo = static_cast<unsigned>(st.v[0][e]) | (static_cast<unsigned>(st.v[1][e]) << 16);
-      const unsigned hi = static_cast<unsigned>(st.v[2][e]) | (static_cast<unsigned>(st.v[3][e]) << 16);
-      *reinterpret_cast<uint2*>(&Vt[b][(dq * 8 + e) * kAVRow + 4 * kq]) = make_uint2(lo, hi);
-    }
-  };
-
-  // ---- one 64-key block for the groups in GM (bit q = group q) ----
-  // LDS fragments are read one MFMA group ahead into alternating registers
-  // (scheduling barriers keep the reads ahead of the MFMAs that hide them).
-  auto process = [&](auto gmc, int b, int kn) __attribute__((always_inline)) {
-    constexpr int gm = decltype(gmc)::value;
-    const unsigned short* kbase = &Ks[b][ln * kAKRow + 8 * lg];
-    const unsigned short* vbase = &Vt[b][ln * kAVRow + 8 * lg];
-    f32x4 st[2][4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) st[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u16x8 kf[2][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kf[0][s] = *reinterpret_cast<const u16x8*>(kbase + 32 * s);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < 3) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          kf[(t + 1) & 1][s] =
-              *reinterpret_cast<const u16x8*>(kbase + 16 * (t + 1) * kAKRow + 32 * s);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          if ((gm >> q) & 1)   // compile-time
-            st[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, kf[t & 1][s]), __builtin_bit_cast(bf16x8, qf[q][s]),
-                st[q][t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // first V fragments go out before the softmax arithmetic
-    u16x8 vf[2][2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) vf[0][s2] = *reinterpret_cast<const u16x8*>(vbase + 32 * s2);
-    // st[q][t][r] = q_row(ln) . k(32(t/2) + 8lg + 4(t%2) + r)
-    bf16x8 phi[2][2], plo[2][2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (!((gm >> q) & 1)) continue;   // compile-time
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + r;
-          st[q][t][r] = key < kn ? st[q][t][r] * scale2 : -INFINITY;
-          bmax = fmaxf(bmax, st[q][t][r]);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
-      const float m_new = fmaxf(m_run[q], bmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
-      m_run[q] = m_new;
-      l_run[q] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) o[q][u] *= alpha;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(st[q][2 * s2 + (j >> 2)][j & 3] - m_new);
-          l_run[q] += pv;
-          const bf16 hi = static_cast<bf16>(pv);
-          phi[q][s2][j] = hi;
-          plo[q][s2][j] = static_cast<bf16>(pv - static_cast<float>(hi));
-        }
-    }
-    // O^T += V^T P^T (P as bf16 hi + lo)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < 7) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          vf[(u + 1) & 1][s2] =
-              *reinterpret_cast<const u16x8*>(vbase + 16 * (u + 1) * kAVRow + 32 * s2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (!((gm >> q) & 1)) continue;   // compile-time
-          const bf16x8 v8 = __builtin_bit_cast(bf16x8, vf[u & 1][s2]);
-          o[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, phi[q][s2], o[q][u], 0, 0, 0);
-          o[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, plo[q][s2], o[q][u], 0, 0, 0);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  const int gm_all = (act[0] ? 1 : 0) | (act[1] ? 2 : 0);
-  using G1 = std::integral_constant<int, 1>;
-  using G2 = std::integral_constant<int, 2>;
-  using G3 = std::integral_constant<int, 3>;
-#define LOPA_PROCESS_GM(GMV, BUF, KN)       \
-  do {                                       \
-    if ((GMV) == 3) process(G3{}, BUF, KN);  \
-    else if ((GMV) == 1) process(G1{}, BUF, KN); \
-    else if ((GMV) == 2) process(G2{}, BUF, KN); \
-  } while (0)
-
-  // ---- phase 1: this split's share of the committed prefix ----
-  const int nbp = (L + kAKB - 1) / kAKB;
-  const int kb_lo = split * nbp / splits;
-  const int kb_hi = (split + 1) * nbp / splits;
-  if (kb_lo < kb_hi) {
-    AttnStage st;
-    {
-      const size_t off = static_cast<size_t>(kb_lo) * kAKB * Hkv * kAD;
-      load_stage(Kp + off, Vp + off, min(kAKB, L - kb_lo * kAKB), st);
-      store_stage(0, st);
-    }
+  // transposed V reads: lane (q = lane/16, i = lane%16) supplies the address of
+  // key k0 + i/4, dims n0 + 4(i%4) .. +4 and receives 4 keys of dim n0 + i
+  const int tq = lane >> 4, ti = lane & 15;
+  const int vkey = 8 * (tq >> 1) + (ti >> 2);          // + 16 t' + 4 hh
+  const int vdim = 16 * (tq & 1) + 4 * (ti & 3);       // + 32 u
+  for (int i = 0; i < n; ++i) {
     __syncthreads();
-    for (int kb = kb_lo; kb < kb_hi; ++kb) {
-      const int cur = (kb - kb_lo) & 1;
-      // the next block's loads stay in flight during this block's MFMAs;
-      // unconditional (the last iteration reloads its own block into the
-      // idle buffer) so the wait lands at the LDS store, not the branch
-      const int nx = min(kb + 1, kb_hi - 1);
-      const size_t off = static_cast<size_t>(nx) * kAKB * Hkv * kAD;
-      load_stage(Kp + off, Vp + off, min(kAKB, L - nx * kAKB), st);
-      __builtin_amdgcn_sched_barrier(0);
-      LOPA_PROCESS_GM(gm_all, cur, min(kAKB, L - kb * kAKB));
-      __builtin_amdgcn_sched_barrier(0);
-      store_stage(cur ^ 1, st);
-      __syncthreads();
+    const unsigned char* Ks = smem + (i % kAStages) * 2 * kAHalf;
+    const unsigned char* Vs = Ks + kAHalf;
+    const int u = u_lo + i;
+    const bool own = u >= nbp;
+    const int v = u - nbp;
+    const int kn = own ? min(kAUnitKeys, B - (v % obp) * kAUnitKeys)
+                       : min(kAUnitKeys, L - u * kAUnitKeys);
+    // rows of another branch see nothing of this branch's own block
+    const bool see = !own || rbr == b_lo + v / obp;
+    // S^T = K Q^T, two 32-key tiles; all 16 K fragments go out first and the
+    // two tiles' accumulation chains interleave
+    u16x8 kf[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 32 * t + kperm(ln);
+      const unsigned char* kb = Ks + kr * kARowBytes;
+      const int sw = aswz(kr);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        kf[t][s] = *reinterpret_cast<const u16x8*>(kb + (((2 * s + lh) ^ sw) << 4));
     }
-  }
-  // ---- phase 2: every branch's own block, seen only by its own rows ----
-  if (split == splits - 1) {
-    const int b_lo = r0 / RB;
-    const int b_hi = min(r0 + kARows - 1, R - 1) / RB;
-    for (int bb = b_lo; bb <= b_hi; ++bb) {
-      const int gm = (gbr[0] == bb ? 1 : 0) | (gbr[1] == bb ? 2 : 0);
-      for (int j0 = 0; j0 < B; j0 += kAKB) {
-        AttnStage st;
-        const size_t off = (static_cast<size_t>(bb) * B + j0) * Hkv * kAD;
-        load_stage(Kb + off, Vb + off, min(kAKB, B - j0), st);
-        store_stage(0, st);
-        __syncthreads();
-        LOPA_PROCESS_GM(gm, 0, min(kAKB, B - j0));
-        __syncthreads();
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t][s]),
+                                                        __builtin_bit_cast(bf16x8, qf[s]), sc[t],
+                                                        0, 0, 0);
+    // V^T fragments of one 16-key PV step: [u2][half]
+    auto vload = [&](int tp, bf16x4 (&va)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int key = 16 * tp + 4 * hh + vkey;
+          const int dim = 32 * u2 + vdim;
+          const int byte = key * kARowBytes + (((dim >> 3) ^ aswz(key)) << 4) + ((dim & 7) << 1);
+          va[u2][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+                  reinterpret_cast<uintptr_t>(Vs + byte)));
+        }
+    };
+    bf16x4 va[2][4][2];
+    vload(0, va[0]);   // in flight during the softmax arithmetic
+    // sc[t][r] = raw score of key 32t + 16(r/8) + 8lh + r%8; keys past kn and
+    // other branches' own blocks are masked (wave-uniform test first)
+    if (__builtin_amdgcn_readfirstlane(kn) < kAUnitKeys || __builtin_amdgcn_ballot_w64(!see) != 0) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + 16 * (r >> 3) + 8 * lh + (r & 7);
+          if (!(see && key < kn)) sc[t][r] = -INFINITY;
+        }
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sc[t][r]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave)) * scale2;
+    // The exponent reference m_ref (log2 units) only moves when a row's block
+    // maximum exceeds it by more than 8, so p <= 2^8 and the rescale of O and
+    // l is skipped for most blocks; O / l is the same for any reference.
+    const bool grow_ref = bmax > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow_ref)) {
+      const float m_new = grow_ref ? bmax : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 when m_ref = -inf
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) o[u2] *= alpha;
+    }
+    // a row that has seen no key yet keeps m_ref = -inf and all p = 0
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // P^T operands of the four 16-key PV steps, as bf16 hi + lo
+    bf16x8 phi[4], plo[4];
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[tp >> 1][8 * (tp & 1) + e], scale2, -m_use));
+        l_run += p;
+        const bf16 hi = static_cast<bf16>(p);
+        phi[tp][e] = hi;
+        plo[tp][e] = static_cast<bf16>(p - static_cast<float>(hi));
       }
+    // O^T += V^T P^T; the next step's V^T fragments are read during this one's MFMAs
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp) {
+      if (tp < 3) vload(tp + 1, va[(tp + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const bf16x8 vf =
+            __builtin_shufflevector(va[tp & 1][u2][0], va[tp & 1][u2][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi[tp], o[u2], 0, 0, 0);
+        o[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo[tp], o[u2], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-#undef LOPA_PROCESS_GM
-
-  // ---- output: o[q][u][r] = O[row ln of group q][dim 16u + 4lg + r] ----
+  // ---- output: o[u][r] = O[row ln][dim 32u + 8(r/4) + 4lh + r%4] ----
+  if (!row_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (splits == 1) {
+    const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (!act[q]) continue;
-    float l_tot = l_run[q] + __shfl_xor(l_run[q], 16, kWave);
-    l_tot += __shfl_xor(l_tot, 32, kWave);
-    if (splits == 1) {
-      const float inv = 1.f / l_tot;
+    for (int u2 = 0; u2 < 4; ++u2)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const unsigned a = f32_to_bf16_bits(o[q][u][0] * inv) |
-                           (static_cast<unsigned>(f32_to_bf16_bits(o[q][u][1] * inv)) << 16);
-        const unsigned c = f32_to_bf16_bits(o[q][u][2] * inv) |
-                           (static_cast<unsigned>(f32_to_bf16_bits(o[q][u][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(H + qoff[q] + 16 * u + 4 * lg) = make_uint2(a, c);
+      for (int a = 0; a < 4; ++a) {
+        const unsigned lo = f32_to_bf16_bits(o[u2][4 * a] * inv) |
+                            (static_cast<unsigned>(f32_to_bf16_bits(o[u2][4 * a + 1] * inv)) << 16);
+        const unsigned hi = f32_to_bf16_bits(o[u2][4 * a + 2] * inv) |
+                            (static_cast<unsigned>(f32_to_bf16_bits(o[u2][4 * a + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(H + qoff + 32 * u2 + 8 * a + 4 * lh) = make_uint2(lo, hi);
       }
-    } else {
-      // partial of row (g, grow + ln): [split][Hkv][rows][128] O, then max, sum
-      const size_t rmax = static_cast<size_t>(nb_max) * RB;
-      const size_t row = (static_cast<size_t>(split) * Hkv + g) * rmax + grow[q] + ln;
-      float* po = part + row * kAD;
+  } else {
+    // partial of row (g, grow): [split][Hkv][rows][128] O, then max, then sum
+    const size_t rmax = static_cast<size_t>(nb_max) * RB;
+    const size_t prow = (static_cast<size_t>(split) * Hkv + g) * rmax + grow;
+    float* po = part + prow * kAD;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4*>(po + 16 * u + 4 * lg) = o[q][u];
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(po + 32 * u2 + 8 * a + 4 * lh) =
+            f32x4{o[u2][4 * a], o[u2][4 * a + 1], o[u2][4 * a + 2], o[u2][4 * a + 3]};
+    if (lh == 0) {
       float* pm = part + static_cast<size_t>(splits) * Hkv * rmax * kAD;
-      if (lg == 0) {
-        pm[row] = m_run[q];
-        pm[static_cast<size_t>(splits) * Hkv * rmax + row] = l_tot;
-      }
+      pm[prow] = m_ref;
+      pm[static_cast<size_t>(splits) * Hkv * rmax + prow] = l_tot;
     }
   }
 }
@@ -449,7 +440,7 @@ extern "C" int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const voi
   const int nb_max = dims->k_max + 1;
   if (p.mfma) {
     const dim3 grid(p.row_groups, dims->Hkv, p.splits);
-    hipLaunchKernelGGL(k_attn_mfma, grid, dim3(256), 0, stream, dims->L, dims->B, dims->Hq,
+    hipLaunchKernelGGL(k_attn_dma, grid, dim3(512), 0, stream, dims->L, dims->B, dims->Hq,
                        dims->Hkv, nb_max, p.splits, nb, static_cast<const unsigned short*>(Kp),
                        static_cast<const unsigned short*>(Vp),
                        static_cast<const unsigned short*>(Qb),

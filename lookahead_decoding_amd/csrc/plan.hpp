@@ -60,10 +60,12 @@ inline size_t lmhead_workspace_bytes(const lopa_dims& d) {
   return static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 12u;
 }
 
-// Attention MFMA kernel (bf16, d = 128, (B * Hq/Hkv) % 16 == 0): workgroups
-// of 128 query rows per KV head; the committed prefix may be split over
-// grid.z when that is the only way to occupy the chip, with the splits'
-// unnormalised partials merged by a second kernel.
+// Attention MFMA kernel (bf16, d = 128): workgroups of 128 query rows per KV
+// head walk work units of 64 keys -- the committed prefix in blocks, then the
+// own block of every branch their rows belong to.  When one pass leaves most
+// compute units idle the units are split over grid.z (at most one workgroup
+// per compute unit, at least two units per split) and a second kernel merges
+// the splits' unnormalised partials.
 constexpr int kAttnRowsPerWG = 128;
 constexpr int kAttnKeysPerBlock = 64;
 
@@ -75,21 +77,17 @@ struct AttnPlan {
 
 inline AttnPlan attn_plan(const lopa_dims& d) {
   AttnPlan p{};
-  const int G = d.Hq / d.Hkv;
-  p.mfma = d.dtype == LOPA_BF16 && d.d == 128 && (d.B * G) % 16 == 0;
+  p.mfma = d.dtype == LOPA_BF16 && d.d == 128;
   p.splits = 1;
   if (!p.mfma) return p;
-  const int rows = (d.k_max + 1) * d.B * G;
+  const int rows = (d.k_max + 1) * d.B * (d.Hq / d.Hkv);
   p.row_groups = (rows + kAttnRowsPerWG - 1) / kAttnRowsPerWG;
   const int wgs = p.row_groups * d.Hkv;
-  const int blocks = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
-  // split only when one pass leaves most compute units idle and every split
-  // keeps at least 8 key blocks
-  if (wgs < 256 && blocks >= 16) {
-    int s = 256 / wgs;
-    if (s > blocks / 8) s = blocks / 8;
-    p.splits = s < 1 ? 1 : s;
-  }
+  const int units = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock +
+                    (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
+  int s = 256 / wgs;
+  if (s > units / 2) s = units / 2;
+  p.splits = s < 1 ? 1 : s;
   return p;
 }
 

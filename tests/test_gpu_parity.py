@@ -138,6 +138,9 @@ ATTN_CASES = [
     ("bf16-mfma-split3", dict(dtype="bf16", L=1500, B=16, m=8, Hq=4, Hkv=1, d=128, k=2), 3),
     ("bf16-mfma-split-nb1", dict(dtype="bf16", L=1100, B=16, m=8, Hq=8, Hkv=2, d=128, k=3), 1),
     ("f32-gqa-d96", dict(L=1030, B=5, m=3, Hq=6, Hkv=3, d=96, k=1), 2),
+    # a full 64-key own block; 32-row tiles straddling branches (B*G = 140)
+    ("bf16-mfma-B64", dict(dtype="bf16", L=200, B=64, m=8, Hq=28, Hkv=4, d=128, k=2), 3),
+    ("bf16-mfma-B20-G7", dict(dtype="bf16", L=64, B=20, m=8, Hq=28, Hkv=4, d=128, k=3), 4),
 ]
 
 
