@@ -27,7 +27,7 @@
 #include <type_traits>
 
 #include "lopa_common.hpp"
-#include "plan.hpp"
+#include "attn_plan.hpp"
 
 namespace lopa {
 

@@ -1,0 +1,52 @@
+// Launch plan of the attention call, shared by its entry point and the
+// workspace query.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "lopa.h"
+
+namespace lopa {
+
+// Attention MFMA kernel (bf16, d = 128): workgroups of 128 query rows per KV
+// head walk work units of 64 keys -- the committed prefix in blocks, then the
+// own block of every branch their rows belong to.  When one pass leaves most
+// compute units idle the units are split over grid.z (at most one workgroup
+// per compute unit, at least two units per split) and a second kernel merges
+// the splits' unnormalised partials.
+constexpr int kAttnRowsPerWG = 128;
+constexpr int kAttnKeysPerBlock = 64;
+
+struct AttnPlan {
+  bool mfma;
+  int row_groups;  // grid.x
+  int splits;      // grid.z
+};
+
+inline AttnPlan attn_plan(const lopa_dims& d) {
+  AttnPlan p{};
+  p.mfma = d.dtype == LOPA_BF16 && d.d == 128;
+  p.splits = 1;
+  if (!p.mfma) return p;
+  const int rows = (d.k_max + 1) * d.B * (d.Hq / d.Hkv);
+  p.row_groups = (rows + kAttnRowsPerWG - 1) / kAttnRowsPerWG;
+  const int wgs = p.row_groups * d.Hkv;
+  const int units = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock +
+                    (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
+  int s = 256 / wgs;
+  if (s > units / 2) s = units / 2;
+  p.splits = s < 1 ? 1 : s;
+  return p;
+}
+
+// Partials of the split prefix: per split, KV head and query row, the
+// unnormalised output (d floats), the running max and the running sum.
+inline size_t attn_workspace_bytes(const lopa_dims& d) {
+  const AttnPlan p = attn_plan(d);
+  if (p.splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(d.k_max + 1) * d.B * (d.Hq / d.Hkv);
+  return static_cast<size_t>(p.splits) * d.Hkv * rows * (d.d + 2) * 4u;
+}
+
+}  // namespace lopa

@@ -26,7 +26,7 @@
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
 #include "lopa_common.hpp"
-#include "plan.hpp"
+#include "head_plan.hpp"
 
 namespace lopa {
 
