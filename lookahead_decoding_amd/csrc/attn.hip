@@ -325,11 +325,14 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
   }
 }
 
-// Merge of the prefix splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// rounded to bf16.  One wave per row (2 dims per lane).
+// Merge of the splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// rounded to bf16.  One wave per row (2 dims per lane); every split's loads
+// are issued before any is used, so the merge costs one memory round trip.
+template <int S>
 __global__ void __launch_bounds__(256)
-k_attn_combine(int B, int Hq, int Hkv, int nb_max, int splits, const int32_t* __restrict__ nb_ptr,
+k_attn_combine(int B, int Hq, int Hkv, int nb_max, const int32_t* __restrict__ nb_ptr,
                const float* __restrict__ part, unsigned short* __restrict__ H) {
+  constexpr int splits = S;
   const int G = Hq / Hkv;
   const int RB = B * G;
   const int nb = min(max(*nb_ptr, 0), nb_max);
@@ -340,16 +343,26 @@ k_attn_combine(int B, int Hq, int Hkv, int nb_max, int splits, const int32_t* __
   const size_t rmax = static_cast<size_t>(nb_max) * RB;
   const float* pm = part + static_cast<size_t>(splits) * Hkv * rmax * kAD;
   const float* pl = pm + static_cast<size_t>(splits) * Hkv * rmax;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pm[(static_cast<size_t>(s) * Hkv + g) * rmax + r]);
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const size_t row = (static_cast<size_t>(s) * Hkv + g) * rmax + r;
-    const float wgt = exp2f(pm[row] - M);   // 0 for a split that saw no key
-    lsum += wgt * pl[row];
-    const float2 ov = *reinterpret_cast<const float2*>(part + row * kAD + 2 * lane);
-    o0 += wgt * ov.x;
-    o1 += wgt * ov.y;
+  // lane s < splits holds split s's (max, sum)
+  const size_t lrow = (static_cast<size_t>(min(lane, splits - 1)) * Hkv + g) * rmax + r;
+  const float ms = lane < splits ? pm[lrow] : -INFINITY;
+  const float ls = lane < splits ? pl[lrow] : 0.f;
+  float2 ov[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    ov[s] = *reinterpret_cast<const float2*>(
+          part + ((static_cast<size_t>(s) * Hkv + g) * rmax + r) * kAD + 2 * lane);
+  float M = ms;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  const float wgt = lane < splits ? exp2f(ms - M) : 0.f;   // 0 for a split that saw no key
+  const float lsum = wave_sum(wgt * ls);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float ws = __shfl(wgt, s, kWave);
+    o0 += ws * ov[s].x;
+    o1 += ws * ov[s].y;
   }
   const float inv = 1.f / lsum;
   const int b = r / RB, rem = r % RB;
@@ -450,9 +463,21 @@ extern "C" int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const voi
     LOPA_LAUNCH_CHECK();
     if (p.splits > 1) {
       const int rows = nb_max * dims->B * (dims->Hq / dims->Hkv);
-      hipLaunchKernelGGL(k_attn_combine, dim3((rows + 3) / 4, dims->Hkv), dim3(256), 0, stream,
-                         dims->B, dims->Hq, dims->Hkv, nb_max, p.splits, nb,
-                         static_cast<const float*>(ws), static_cast<unsigned short*>(H));
+      const dim3 cg((rows + 3) / 4, dims->Hkv);
+      const float* pw = static_cast<const float*>(ws);
+      unsigned short* Hw = static_cast<unsigned short*>(H);
+      switch (p.splits) {
+#define LOPA_COMBINE(S)                                                                      \
+  case S:                                                                                    \
+    hipLaunchKernelGGL(k_attn_combine<S>, cg, dim3(256), 0, stream, dims->B, dims->Hq,       \
+                       dims->Hkv, nb_max, nb, pw, Hw);                                       \
+    break;
+        LOPA_COMBINE(2) LOPA_COMBINE(3) LOPA_COMBINE(4) LOPA_COMBINE(5) LOPA_COMBINE(6)
+        LOPA_COMBINE(7) LOPA_COMBINE(8) LOPA_COMBINE(9) LOPA_COMBINE(10) LOPA_COMBINE(11)
+        LOPA_COMBINE(12) LOPA_COMBINE(13) LOPA_COMBINE(14) LOPA_COMBINE(15) LOPA_COMBINE(16)
+#undef LOPA_COMBINE
+        default: return LOPA_ERR_UNSUPPORTED;
+      }
       LOPA_LAUNCH_CHECK();
     }
     return LOPA_OK;

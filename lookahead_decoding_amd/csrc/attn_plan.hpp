@@ -13,10 +13,11 @@ namespace lopa {
 // head walk work units of 64 keys -- the committed prefix in blocks, then the
 // own block of every branch their rows belong to.  When one pass leaves most
 // compute units idle the units are split over grid.z (at most one workgroup
-// per compute unit, at least two units per split) and a second kernel merges
-// the splits' unnormalised partials.
+// per compute unit, at least two units per split, at most kAttnMaxSplits)
+// and a second kernel merges the splits' unnormalised partials.
 constexpr int kAttnRowsPerWG = 128;
 constexpr int kAttnKeysPerBlock = 64;
+constexpr int kAttnMaxSplits = 16;
 
 struct AttnPlan {
   bool mfma;
@@ -36,6 +37,7 @@ inline AttnPlan attn_plan(const lopa_dims& d) {
                     (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
   int s = 256 / wgs;
   if (s > units / 2) s = units / 2;
+  if (s > kAttnMaxSplits) s = kAttnMaxSplits;
   p.splits = s < 1 ? 1 : s;
   return p;
 }

@@ -102,16 +102,31 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
                 int32_t* __restrict__ arg_next) {
   const int p = threadIdx.x;
   const bool live = p < B;
+  const int pc = live ? p : B - 1;   // in-bounds index for idle lanes
   const int nb = *nb_ptr;
+  // every slot's flag and confidence is fetched before any is used
+  uint8_t mk[LOPA_MAX_BRANCHES];
+  float cf[LOPA_MAX_BRANCHES];
+  int32_t tk[LOPA_MAX_BRANCHES], ag[LOPA_MAX_BRANCHES];
+#pragma unroll
+  for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) {
+    const int bb = b < nb_max ? b : nb_max - 1;
+    mk[b] = br_mask[bb * B + pc];
+    cf[b] = conf[bb * B + pc];
+    tk[b] = br_tok[bb * B + pc];
+    ag[b] = arg[bb * B + pc];
+  }
   float best = 0.f;
   int w = 0;
-  for (int b = 0; b < nb_max; ++b) {
+#pragma unroll
+  for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) {
+    if (b >= nb_max) break;
     float bc = -1.f;
     if (b < nb) {
-      const bool m = live && br_mask[b * B + p] != 0;
-      const float s = wave_sum(m ? conf[b * B + p] : 0.f);
+      const bool m = live && mk[b] != 0;
+      const float sm = wave_sum(m ? cf[b] : 0.f);
       const int n = __popcll(__ballot(m));
-      bc = n ? s / static_cast<float>(n) : 1.f;
+      bc = n ? sm / static_cast<float>(n) : 1.f;
       if (b == 0 || bc > best) {
         best = bc;
         w = b;
@@ -119,11 +134,22 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
     }
     if (p == 0) bconf[b] = bc;
   }
+  // the winner's slot, picked from registers (w is wave-uniform)
+  bool m = false;
+  float cw = 0.f;
+  int32_t tw = 0, aw = 0;
+#pragma unroll
+  for (int b = 0; b < LOPA_MAX_BRANCHES; ++b)
+    if (b == w) {
+      m = mk[b] != 0;
+      cw = cf[b];
+      tw = tk[b];
+      aw = ag[b];
+    }
   if (live) {
-    const bool m = br_mask[w * B + p] != 0;
-    tok_next[p] = br_tok[w * B + p];
-    conf_next[p] = m ? conf[w * B + p] : 0.f;
-    arg_next[p] = m ? arg[w * B + p] : -1;
+    tok_next[p] = tw;
+    conf_next[p] = m ? cw : 0.f;
+    arg_next[p] = m ? aw : -1;
   }
   if (p == 0) winner[0] = w;
 }
