@@ -11,13 +11,11 @@ namespace lopa {
 
 // MFMA kernel (bf16, hidden % 64 == 0): one launch of kHeadParts persistent
 // workgroups, one per compute unit of an MI355X.  The device-side row count
-// M picks the layout (head_groups): up to kHeadSmallRows rows, every
-// workgroup owns a balanced contiguous vocabulary range and all rows; above
-// that the rows are split into at most kHeadGroupTiles 32-row tiles per
-// group, and the groups of one vocabulary range run side by side on the same
-// XCD so the weight crosses HBM once.
+// M picks the layout (head_groups): with few rows every workgroup owns a
+// balanced contiguous vocabulary range and all rows; with many the rows are
+// split into groups, and the groups of one vocabulary range run side by side
+// on the same XCD so the weight crosses HBM once.
 constexpr int kHeadParts = 256;
-constexpr int kHeadSmallRows = 128;
 constexpr int kHeadGroupTiles = 8;
 // Plain kernel (float32, or shapes outside the MFMA kernel): one vocabulary
 // entry per thread, 256 per workgroup.
@@ -38,19 +36,37 @@ inline HeadPlan head_plan(const lopa_dims& d) {
   return p;
 }
 
-// Row groups of the MFMA kernel for M rows.  wide: 2x2 compute-wave layout
-// (vocabulary x rows) instead of 4x1; groups: row groups; nparts: vocabulary
-// parts per group (a multiple of the 8 XCDs, nparts * groups <= kHeadParts);
-// tpg: 32-row tiles per group.  m_max <= 1024 keeps groups <= 4.
+// Row groups of the MFMA kernel for M rows (in 32-row tiles).  wide: the
+// 2 x 4 compute-wave layout (128 vocabulary rows x 256 rows per pass) instead
+// of 4 x 2 (256 x 128); groups: row groups, whose workgroups stream the same
+// vocabulary part side by side; nparts: vocabulary parts per group (a
+// multiple of the 8 XCDs, nparts * groups <= kHeadParts); tpg: tiles per
+// group.  Each choice below takes the fewest K chunks per workgroup (one
+// chunk costs about the same in either layout), the fewer groups on a tie:
+// <= 4 tiles: one group, 4 x 2; 5..8: one group, 2 x 4; 9..12: three groups
+// of <= 4 tiles, 4 x 2; more: groups of <= 8 tiles, 2 x 4.  m_max <= 1024
+// keeps groups <= 4.
 struct HeadGroups {
   int wide, groups, nparts, tpg;
 };
 
 __host__ __device__ inline HeadGroups head_groups(int M) {
   const int tiles = (M + 31) / 32;
-  if (M <= kHeadSmallRows) return HeadGroups{0, 1, kHeadParts, tiles};
-  const int g = (tiles + kHeadGroupTiles - 1) / kHeadGroupTiles;
-  return HeadGroups{1, g, 8 * (kHeadParts / 8 / g), (tiles + g - 1) / g};
+  int wide, g;
+  if (tiles <= 4) {
+    wide = 0;
+    g = 1;
+  } else if (tiles <= 8) {
+    wide = 1;
+    g = 1;
+  } else if (tiles <= 12) {
+    wide = 0;
+    g = 3;
+  } else {
+    wide = 1;
+    g = (tiles + kHeadGroupTiles - 1) / kHeadGroupTiles;
+  }
+  return HeadGroups{wide, g, 8 * (kHeadParts / 8 / g), (tiles + g - 1) / g};
 }
 
 // Per (row, vocabulary tile) partial: max logit (float), scaled sum (float),

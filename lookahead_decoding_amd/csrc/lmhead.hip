@@ -17,12 +17,12 @@
 //                   row of its row group.  Four producer waves move 64-wide
 //                   K chunks of W and H straight from HBM/L2 into a
 //                   three-stage XOR-swizzled LDS ring with buffer loads that
-//                   write LDS; four compute waves read
+//                   write LDS; eight compute waves (two per SIMD) read
 //                   v_mfma_f32_32x32x16_bf16 fragments from it.  W is read
 //                   from HBM exactly once.  The row count M lives on the
-//                   device and picks the body: all rows in one group up to
-//                   128, else groups of up to 256 rows whose workgroups
-//                   share the weight stream through L2.
+//                   device and picks the body and the row groups; the
+//                   groups of one vocabulary range share the weight stream
+//                   through L2.
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
 #include "lopa_common.hpp"
@@ -79,12 +79,16 @@ constexpr int kKC = 64;          // K chunk
 constexpr int kRB = kKC * 2;     // bytes of one row per chunk (8 slots of 16 B)
 constexpr int kStages = 3;       // LDS stages: S - 1 chunks in flight while one is computed
 constexpr int kRunRows = 512;    // running partials: compute-wave columns x rows
+constexpr int kComputeWaves = 8; // two per SIMD, so one wave's LDS reads hide under the other's MFMAs
+constexpr int kLoadWaves = 4;
+constexpr int kHeadThreads = 64 * (kComputeWaves + kLoadWaves);
 
-// Shape of one body: WX x (4 / WX) compute waves over (vocabulary, rows);
-// each wave holds NVW 32-row vocabulary tiles against MTW 32-row tiles of H.
+// Shape of one body: WX x (kComputeWaves / WX) compute waves over
+// (vocabulary, rows); each wave holds NVW 32-row vocabulary tiles against MTW
+// 32-row tiles of H.
 template <int WX, int NVW, int MTW>
 struct HeadTile {
-  static constexpr int WY = 4 / WX;
+  static constexpr int WY = kComputeWaves / WX;
   static constexpr int WROWS = WX * NVW * 32;       // vocabulary rows per pass
   static constexpr int HROWS = WY * MTW * 32;       // LM-head rows staged per chunk
   static constexpr int BUF = (WROWS + HROWS) * kRB; // bytes per LDS stage
@@ -110,15 +114,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // walks the range in passes of WROWS vocabulary rows, each pass the full
 // hidden dimension in 64-wide K chunks.
 //
-// Warp-specialised, 512 threads.  Waves 4..7 only issue loads: each 128-byte
+// Warp-specialised, 768 threads.  Waves 8..11 only issue loads: each 128-byte
 // row segment of a chunk is fetched by 8 lanes with 16-byte buffer loads
 // that write straight into LDS (no registers on the way), 8 rows per
 // instruction, in the XOR-swizzled order the fragment reads expect.  Three
 // LDS stages: while the compute waves work on chunk i, chunks i+1 and i+2 are
 // in flight; the producers issue chunk i+2 once the barrier that ends chunk
 // i-1 shows its stage is free, and wait for chunk i+1 to land before the
-// next barrier.  Waves 0..3 only compute: v_mfma_f32_32x32x16_bf16 with the
-// A operand from W and the B operand from H, fragments read from LDS.  After
+// next barrier.  Waves 0..7 only compute, two per SIMD:
+// v_mfma_f32_32x32x16_bf16 with the A operand from W and the B operand from
+// H, fragments read from LDS.  After
 // each pass a wave folds its logits into a running (max, sum, argmax) per
 // row in LDS; at the end the wave columns are merged and one partial per row
 // is written.  W is addressed through a buffer descriptor covering exactly
@@ -151,12 +156,12 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   const int rot = ((part >> 3) * nch / 32) % nch;
 
   Partial* run = reinterpret_cast<Partial*>(smem + kStages * kHeadStage);
-  for (int r = tid; r < kRunRows; r += 512) run[r] = empty_partial();
+  for (int r = tid; r < kRunRows; r += kHeadThreads) run[r] = empty_partial();
   __syncthreads();
 
-  if (w >= 4) {
+  if (w >= kComputeWaves) {
     // ---------------- producer waves ----------------
-    const int pw = w - 4;
+    const int pw = w - kComputeWaves;
     const int r8 = lane >> 3;                    // row within an 8-row load
     const int ls = (lane & 7) ^ r8 ^ (pw & 1);   // logical slot landing in physical slot lane & 7
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -271,7 +276,7 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     }
   }
   __syncthreads();
-  for (int r = tid; r < Mg; r += 512) {
+  for (int r = tid; r < Mg; r += kHeadThreads) {
     Partial p = run[r];
 #pragma unroll
     for (int x = 1; x < WX; ++x) p = merge(p, run[x * T::RUNS + r]);
@@ -282,11 +287,11 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   }
 }
 
-// kHeadParts workgroups of 512 threads, one per compute unit.  Block b sits
+// kHeadParts workgroups of 768 threads, one per compute unit.  Block b sits
 // on XCD b % 8; the row groups of one vocabulary part take consecutive
 // blocks of the same XCD, so they stream the same weight lines together and
 // the second reader is served from that XCD's L2 (or the MALL behind it).
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(kHeadThreads)
 k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
               const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
@@ -306,17 +311,15 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
   const int Mg = min(M - row0, g.tpg * 32);
 #define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
                   logits_out
+  // up to 4 tiles: 4 x 2 compute waves (256 vocabulary rows per pass);
+  // 5..8 tiles: 2 x 4 compute waves (128 vocabulary rows per pass)
+  // the weight is read non-temporally unless other row groups share it
   if (!g.wide) {
-    switch (g.tpg) {
-      case 1: head_body<4, 2, 1, 2>(LOPA_ARGS); break;
-      case 2: head_body<4, 2, 2, 2>(LOPA_ARGS); break;
-      case 3: head_body<4, 2, 3, 2>(LOPA_ARGS); break;
-      default: head_body<4, 2, 4, 2>(LOPA_ARGS); break;
-    }
-  } else if (g.tpg <= 6) {
-    head_body<2, 2, 3, 0>(LOPA_ARGS);
+    if (g.groups > 1) head_body<4, 2, 2, 0>(LOPA_ARGS);
+    else if (g.tpg <= 2) head_body<4, 2, 1, 2>(LOPA_ARGS);
+    else head_body<4, 2, 2, 2>(LOPA_ARGS);
   } else {
-    head_body<2, 2, 4, 0>(LOPA_ARGS);
+    head_body<2, 2, 2, 0>(LOPA_ARGS);
   }
 #undef LOPA_ARGS
 }
@@ -417,7 +420,7 @@ extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void
   const unsigned short* Wb = static_cast<const unsigned short*>(W);
   const int h_bytes = p.m_max * hidden * 2;   // H is [nb_max][B][hidden]
   if (p.mfma) {
-    hipLaunchKernelGGL(k_lmhead_mfma, dim3(kHeadParts), dim3(512), 0, stream, V, hidden, nb_max,
+    hipLaunchKernelGGL(k_lmhead_mfma, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V, hidden, nb_max,
                        p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi, logits_out);
   } else {
     const dim3 grid(p.ntiles, p.m_max);

@@ -174,6 +174,9 @@ HEAD_CASES = [
     ("bf16-stream-12tiles", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=1000, B=32, m=30, k=5), None),
     ("bf16-stream-1row", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=3001, B=8, m=1, k=0), None),
     ("bf16-tiled-hidden192", dict(dtype="bf16", Hq=3, Hkv=1, d=64, V=777, B=16, m=15, k=2), None),
+    # 300 rows: three row groups of <= 4 tiles; 450 rows: two groups of <= 8 tiles
+    ("bf16-three-groups", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=2500, B=32, m=30, k=9), None),
+    ("bf16-two-wide-groups", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=1900, B=64, m=50, k=8), None),
 ]
 
 
