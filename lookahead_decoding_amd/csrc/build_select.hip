@@ -27,38 +27,28 @@ k_branch_build(int B, int nb_max, int k, float tau,
   const float c = live ? conf[p] : 0.f;
   const int a = live ? arg[p] : 0;
   const bool masked = live && t == LOPA_MASK_TOKEN;
-
-  // Anchor: every masked position strictly above tau ...
-  bool fill = masked && c > tau;
-  const unsigned long long any_masked = __ballot(masked);
-  if (__ballot(fill) == 0ull && any_masked != 0ull) {
-    // ... else the single most confident masked position (lowest p on a tie).
-    float bv = masked ? c : 0.f;
-    int bi = masked ? p : 0x7fffffff;
-    bool bok = masked;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool ook = __shfl_xor(static_cast<int>(bok), o, kWave) != 0;
-      if (ook && (!bok || better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-        bok = true;
-      }
-    }
-    fill = (p == bi);
+  const unsigned long long mask_bits = __ballot(masked);
+  // rank of each masked position among all masked positions by (confidence
+  // desc, position asc); the position index is wave-uniform, so the other
+  // lanes' confidences come through v_readlane, not LDS
+  const int cbits = __float_as_int(c);
+  int rank = 0;
+  for (int q = 0; q < B; ++q) {
+    const float cq = __int_as_float(__builtin_amdgcn_readlane(cbits, q));
+    if (((mask_bits >> q) & 1ull) && (cq > c || (cq == c && q < p))) ++rank;
   }
+  // Anchor: every masked position strictly above tau, else the single most
+  // confident masked position (rank 0, lowest p on a tie).
+  bool fill = masked && c > tau;
+  if (__ballot(fill) == 0ull) fill = masked && rank == 0;
+  const int n_fill = __popcll(__ballot(fill));
   const bool remaining = masked && !fill;
   const unsigned long long rem_bits = __ballot(remaining);
   const int n_rem = __popcll(rem_bits);
-
-  // Rank of each remaining position by (confidence desc, position asc).
-  int rank = 0;
-  for (int q = 0; q < B; ++q) {
-    const float cq = __shfl(c, q, kWave);
-    if (((rem_bits >> q) & 1ull) && (cq > c || (cq == c && q < p))) ++rank;
-  }
+  // every filled position is more confident than every remaining one (above
+  // tau against at most tau, or the overall first), so among the remaining
+  // positions the rank drops by the fill count
+  rank -= n_fill;
   const int k_eff = k < n_rem ? k : n_rem;
   const int nb = 1 + k_eff;
   const int my_branch = (remaining && rank < k_eff) ? rank + 1 : 0;  // 0: not a lookahead pos
@@ -116,6 +106,24 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
     tk[b] = br_tok[bb * B + pc];
     ag[b] = arg[bb * B + pc];
   }
+  // every slot's sum over its still-masked positions, all reduced together
+  // (one butterfly: six cross-lane steps in total, not six per slot)
+  float sm[LOPA_MAX_BRANCHES];
+  int cnt[LOPA_MAX_BRANCHES];
+#pragma unroll
+  for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) {
+    const bool m = live && mk[b] != 0;
+    sm[b] = m ? cf[b] : 0.f;
+    cnt[b] = __popcll(__ballot(m));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float x[LOPA_MAX_BRANCHES];
+#pragma unroll
+    for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) x[b] = __shfl_xor(sm[b], o, kWave);
+#pragma unroll
+    for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) sm[b] += x[b];
+  }
   float best = 0.f;
   int w = 0;
 #pragma unroll
@@ -123,10 +131,7 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
     if (b >= nb_max) break;
     float bc = -1.f;
     if (b < nb) {
-      const bool m = live && mk[b] != 0;
-      const float sm = wave_sum(m ? cf[b] : 0.f);
-      const int n = __popcll(__ballot(m));
-      bc = n ? sm / static_cast<float>(n) : 1.f;
+      bc = cnt[b] ? sm[b] / static_cast<float>(cnt[b]) : 1.f;
       if (b == 0 || bc > best) {
         best = bc;
         w = b;
