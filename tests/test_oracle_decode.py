@@ -1,0 +1,136 @@
+"""Pins of the block-decoding oracle (oracle/decode_oracle.py).
+
+* Philox4x32-10 against the known-answer vectors published with the
+  generator (Random123 distribution, kat_vectors: philox4x32 with 10 rounds).
+* The Irwin-Hall values: exact multiples of 2^-16 inside [-6, 6], and the
+  moments of a sum of twelve uniforms (mean 0, variance 1, excess kurtosis
+  -1/10) -- a sum of eight, or halves taken from one draw twice, fails them.
+* Token keying: the same token at the same position gives the same vectors
+  in every branch, anything else differs.
+* The decoding loop against cases with closed-form outcomes and invariants.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import decode_oracle as D
+from oracle import lopa_oracle as O
+
+KAT = [  # (counter, key, output) -- Random123 kat_vectors, philox4x32 R = 10
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,out", KAT)
+def test_philox_known_answers(ctr, key, out):
+    got = D.philox4x32_10(np.array(ctr, np.uint32), np.array(key, np.uint32))
+    assert tuple(int(x) for x in got) == out
+
+
+def test_philox_vectorised_matches_scalar():
+    rng = np.random.default_rng(5)
+    ctr = rng.integers(0, 2**32, size=(50, 4), dtype=np.uint64).astype(np.uint32)
+    key = np.array([0x12345678, 0x9abcdef0], np.uint32)
+    batch = D.philox4x32_10(ctr, key)
+    for i in range(50):
+        assert np.array_equal(batch[i], D.philox4x32_10(ctr[i], key))
+
+
+def _values(n=200_000, seed=3):
+    tok = np.zeros((1, 1), np.int64)
+    vals = []
+    for kind in range(3):
+        x = D.synth_values(seed, kind, 1, tok, n // 3, dtype=np.float32).astype(np.float64)
+        vals.append(x.ravel())
+    return np.concatenate(vals)
+
+
+def test_irwin_hall_exact_grid_and_range():
+    x = _values(30_000)
+    assert np.all(x >= -6) and np.all(x < 6)
+    assert np.all(x * 65536 == np.round(x * 65536))
+
+
+def test_irwin_hall_moments():
+    x = _values()
+    n = x.size
+    assert abs(x.mean()) < 5 / np.sqrt(n)
+    assert abs(x.var() - 1.0) < 0.02
+    kurt = np.mean((x - x.mean()) ** 4) / x.var() ** 2 - 3.0
+    assert abs(kurt - (-0.1)) < 0.05
+
+
+def test_bf16_values_round_the_exact_ones():
+    tok = np.array([[3, -1, 7]])
+    exact = D.synth_values(11, D.KIND_K, 2, tok, 16, dtype=np.float32).astype(np.float64)
+    bits = D.synth_values(11, D.KIND_K, 2, tok, 16, dtype=np.uint16)
+    assert np.array_equal(bits, O.f64_to_bf16(exact))
+
+
+def test_token_keying():
+    tok = np.array([[5, -1, 9, 9], [5, 4, 9, 2]])
+    Q, K, V = D.token_qkv(7, tok, 4, 2, 32)
+    assert Q.shape == (2, 4, 4, 32) and K.shape == (2, 4, 2, 32) and V.shape == K.shape
+    for A in (Q, K, V):
+        assert np.array_equal(A[0, 0], A[1, 0])          # same token, same position
+        assert np.array_equal(A[0, 2], A[1, 2])
+        assert not np.array_equal(A[0, 1], A[1, 1])      # masked vs token 4
+        assert not np.array_equal(A[0, 3], A[1, 3])      # 9 vs 2
+        assert not np.array_equal(A[0, 2], A[0, 3])      # same token, other position
+    assert not np.array_equal(K, V)                       # the tensor enters the key
+    Q2, _, _ = D.token_qkv(8, tok, 4, 2, 32)
+    assert not np.array_equal(Q, Q2)                      # the seed enters the key
+
+
+def _inp(**kw):
+    base = dict(dtype="bf16", L=40, B=16, m=10, k=3, Hq=4, Hkv=2, d=32, V=600)
+    base.update(kw)
+    return synth.make_inputs(synth.TINY, **base)
+
+
+def test_decode_fills_every_position_and_never_changes_filled_ones():
+    inp = _inp()
+    tr = D.decode_block(inp, seed=21, k=3, tau=0.9)
+    tok = tr.tok0.copy()
+    for st in tr.steps:
+        assert st.filled >= 1
+        kept = tok != O.MASK
+        assert np.array_equal(st.tok[kept], tok[kept])
+        tok = st.tok
+    assert not np.any(tok == O.MASK)
+    assert len(tr.steps) <= int(np.sum(tr.tok0 == O.MASK))
+    assert 1 <= len(tr.steps)
+
+
+def test_decode_threshold_below_every_confidence_fills_all_in_one_step():
+    # tau < 0: the anchor fills every masked position with the initial pass's
+    # argmax, in one step
+    inp = _inp()
+    tr = D.decode_block(inp, seed=4, k=2, tau=-1.0)
+    assert len(tr.steps) == 1
+    m = tr.tok0 == O.MASK
+    assert np.array_equal(tr.steps[0].tok[m], tr.arg0[m])
+
+
+def test_decode_unreachable_threshold_without_lookahead_fills_one_per_step():
+    # tau > 1 and k = 0: only the fallback fill, one position per step, in the
+    # order of the confidences each step reports
+    inp = _inp(m=6)
+    tr = D.decode_block(inp, seed=9, k=0, tau=2.0)
+    assert len(tr.steps) == 6
+    assert all(st.filled == 1 and st.nb == 1 and st.winner == 0 for st in tr.steps)
+    assert tr.tpf == 1.0
+
+
+def test_decode_lookahead_never_slower_than_one_per_step():
+    inp = _inp(k=4)
+    tr = D.decode_block(inp, seed=33, k=4, tau=2.0)
+    # with tau unreachable each step fills 1 (anchor) or 2 (a lookahead branch wins)
+    assert all(st.filled in (1, 2) for st in tr.steps)
+    assert all((st.filled == 2) == (st.winner > 0) for st in tr.steps)
+    assert tr.tpf >= 1.0
