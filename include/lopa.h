@@ -178,6 +178,29 @@ int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
                        float* bconf, int32_t* winner, int32_t* tok_next,
                        float* conf_next, int32_t* arg_next, hipStream_t stream);
 
+/*
+ * Token-keyed synthetic projections, for decoding a whole block over several
+ * steps without a model: the news article above (section "LoPA 的核心设计：
+ * 前瞻并行与分支验证") repeats explore / verify / select until the block is
+ * decoded, and each verification pass sees every branch's own tokens.  This
+ * call stands in for the projections a model would compute from them.
+ * For every slot b < nb, position p, head h and dimension e:
+ *   value = (sum of twelve 16-bit uniforms) / 2^16 - 6
+ * with the uniforms taken from two Philox4x32-10 draws (Salmon, Moraes, Dror,
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) under key
+ * (seed low 32 bits, seed high 32 bits) and counters
+ * (p | kind << 8 | h << 16, br_tok[b*B+p] as uint32, e, draw), kind 0/1/2 for
+ * Q/K/V: all 8 halves of draw 0's words, then the low and high halves of
+ * draw 1's words 0 and 1.  Values are exact in float32; bf16 output rounds
+ * them to nearest, ties to even.  Two slots holding the same token at p get
+ * the same vectors there.
+ * In  seed; br_tok[nb_max*B] (e.g. as written by lopa_branch_build); nb[1]
+ * Out Qb [nb_max][B][Hq][d], Kb and Vb [nb_max][B][Hkv][d] in dims->dtype;
+ *     slots b >= nb are not written.
+ */
+int lopa_synth_qkv(const lopa_dims* dims, uint64_t seed, const int32_t* br_tok,
+                   const int32_t* nb, void* Qb, void* Kb, void* Vb, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,8 @@ _SIGS = {
                          ctypes.c_int),
     "lopa_branch_select": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                            ctypes.c_int),
+    "lopa_synth_qkv": ([ctypes.POINTER(Dims), ctypes.c_uint64, _P, _P, _P, _P, _P, _P],
+                       ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -178,6 +180,16 @@ def lopa_branch_select(dims, nb, br_mask, br_tok, conf, arg, bconf, winner, tok_
         _ptr(br_tok, i32, "br_tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
         _ptr(bconf, f32, "bconf"), _ptr(winner, i32, "winner"), _ptr(tok_next, i32, "tok_next"),
         _ptr(conf_next, f32, "conf_next"), _ptr(arg_next, i32, "arg_next"), _stream(stream)))
+
+
+def lopa_synth_qkv(dims, seed, br_tok, nb, Qb, Kb, Vb, stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    i32 = torch.int32
+    _check("lopa_synth_qkv", lib().lopa_synth_qkv(
+        ctypes.byref(dims), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(br_tok, i32, "br_tok"),
+        _ptr(nb, i32, "nb"), _ptr(Qb, a, "Qb"), _ptr(Kb, a, "Kb"), _ptr(Vb, a, "Vb"),
+        _stream(stream)))
 
 
 from .step import StepBuffers, run_step, initial_pass  # noqa: E402,F401

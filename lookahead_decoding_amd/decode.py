@@ -1,0 +1,94 @@
+"""Decoding one block over several LoPA steps on the device (plumbing only).
+
+The news article "上交大 × 华为小艺推出LoPA：7B扩散语言模型单样例1000+ tokens/s！"
+(section "LoPA 的核心设计：前瞻并行与分支验证") repeats explore, verify and
+select, reusing the winner's verification outputs, until the block is
+decoded.  This module only sequences library calls on one stream: an initial
+pass of the block as it stands, then per step lopa_branch_build ->
+lopa_synth_qkv (the token-keyed stand-in for the model's projections of every
+branch) -> lopa_branch_attn -> lopa_lmhead_conf -> lopa_branch_select, with the
+state (tokens, confidence, argmax) ping-ponged between two device buffers and
+never read back by the host.  A step taken after the block is complete
+changes nothing (no position is masked, so nothing is filled).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_select,
+               lopa_lmhead_conf, lopa_synth_qkv)
+from .step import StepBuffers
+
+
+class DecodeBuffers(StepBuffers):
+    """StepBuffers plus the per-branch projections and a second state."""
+
+    def __init__(self, dims, device="cuda"):
+        import torch
+        super().__init__(dims, device)
+        act = torch.float32 if dims.dtype == 0 else torch.bfloat16
+        nbm, B = dims.nb_max, dims.B
+        self.Qb = torch.zeros(nbm, B, dims.Hq, dims.d, dtype=act, device=device)
+        self.Kb = torch.zeros(nbm, B, dims.Hkv, dims.d, dtype=act, device=device)
+        self.Vb = torch.zeros_like(self.Kb)
+        self.one = torch.ones(1, dtype=torch.int32, device=device)
+        # state a step reads: tokens [B], confidence [B], argmax [B]
+        self.tok = torch.zeros(B, dtype=torch.int32, device=device)
+        self.conf_s = torch.zeros(B, dtype=torch.float32, device=device)
+        self.arg_s = torch.zeros(B, dtype=torch.int32, device=device)
+        self.rows0 = torch.zeros(nbm * B, dtype=torch.int32, device=device)
+        self.row_ptr0 = torch.zeros(nbm + 1, dtype=torch.int32, device=device)
+
+    def swap_state(self):
+        self.tok, self.tok_next = self.tok_next, self.tok
+        self.conf_s, self.conf_next = self.conf_next, self.conf_s
+        self.arg_s, self.arg_next = self.arg_next, self.arg_s
+
+
+def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None) -> None:
+    """Load the block ``tok0`` (host int32 [B], MASK where masked) and run the
+    initial pass: slot 0's projections, attention, and the LM head on every
+    masked position, which gives the state the first step starts from."""
+    import torch
+    tok0 = np.asarray(tok0, np.int32)
+    dev = buf.tok.device
+    B = dims.B
+    buf.tok.copy_(torch.from_numpy(tok0).to(dev))
+    masked = np.flatnonzero(tok0 == MASK).astype(np.int32)
+    buf.rows0.zero_()
+    buf.rows0[:len(masked)] = torch.from_numpy(masked).to(dev)
+    buf.row_ptr0.fill_(len(masked))
+    buf.row_ptr0[0] = 0
+    lopa_synth_qkv(dims, seed, buf.tok, buf.one, buf.Qb, buf.Kb, buf.Vb, stream)
+    lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.one, buf.H, buf.ws, stream)
+    buf.conf.zero_()
+    buf.arg.fill_(-1)
+    lopa_lmhead_conf(dims, buf.H, W, buf.rows0, buf.row_ptr0, buf.one, buf.conf, buf.arg, None,
+                     buf.ws, stream)
+    buf.conf_s.copy_(buf.conf[:B])
+    buf.arg_s.copy_(buf.arg[:B])
+
+
+def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None) -> None:
+    """One explore / verify / select step on the current state, then swap in
+    the winner's state."""
+    lopa_branch_build(dims, k, tau, buf.tok, buf.conf_s, buf.arg_s, buf.nb, buf.br_tok,
+                      buf.br_mask, buf.rows, buf.row_ptr, stream)
+    lopa_synth_qkv(dims, seed, buf.br_tok, buf.nb, buf.Qb, buf.Kb, buf.Vb, stream)
+    lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.nb, buf.H, buf.ws, stream)
+    lopa_lmhead_conf(dims, buf.H, W, buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg, None,
+                     buf.ws, stream)
+    lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
+                       buf.winner, buf.tok_next, buf.conf_next, buf.arg_next, stream)
+    buf.swap_state()
+
+
+def decode_block(dims, k, tau, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, steps: int,
+                 log=None, stream=None) -> None:
+    """The initial pass and ``steps`` steps; ``log`` (device int32
+    [steps][B]) receives the tokens after each step."""
+    start_block(dims, seed, tok0, Kp, Vp, W, buf, stream)
+    for s in range(steps):
+        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream)
+        if log is not None:
+            log[s].copy_(buf.tok)

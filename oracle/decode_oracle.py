@@ -136,8 +136,10 @@ class DecodeStep:
     winner: int
     tok: np.ndarray          # [B] after the step
     filled: int              # positions filled by the step
-    tok_margin: float        # smallest top-2 logit gap among the rows the step listed
-    rank_gap: float          # smallest confidence gap the explore stage ranked on
+    # how clear-cut the step's decisions were (for comparing with an
+    # implementation that rounds differently):
+    fill_margin: float       # smallest top-2 logit gap behind a token the step filled
+    rank_gap: float          # smallest confidence gap the explore stage's choices hinged on
     tau_gap: float           # smallest |confidence - tau| over masked positions
     win_margin: float        # best minus second-best branch confidence
 
@@ -170,13 +172,28 @@ def block_inputs(inp, seed: int, tokens: np.ndarray):
                    Kb=_pad(K, cfg.nb_max), Vb=_pad(V, cfg.nb_max))
 
 
-def _gaps(tok, conf, tau):
+def _explore_gaps(tok, conf, tau, k):
+    """Confidence gaps the explore stage's choices depend on: the threshold
+    test of every masked position, the fallback's top-1 against top-2 when
+    nothing passes it, and the order of the k+1 most confident positions
+    the anchor leaves (which of them the lookahead branches fill)."""
     m = np.flatnonzero(tok == MASK)
     if m.size == 0:
         return np.inf, np.inf
-    c = np.sort(conf[m].astype(np.float64))
-    rank_gap = float(np.min(np.diff(c))) if c.size > 1 else np.inf
-    return rank_gap, float(np.min(np.abs(c - tau)))
+    c = conf.astype(np.float64)
+    tau_gap = float(np.min(np.abs(c[m] - tau)))
+    above = [p for p in m if c[p] > tau]
+    gaps = []
+    order = sorted(m, key=lambda p: (-c[p], p))
+    if not above:
+        if len(order) > 1:
+            gaps.append(c[order[0]] - c[order[1]])
+        fill = [order[0]]
+    else:
+        fill = above
+    rest = [p for p in order if p not in fill][:k + 1]
+    gaps += [c[a] - c[b] for a, b in zip(rest, rest[1:])]
+    return (float(min(gaps)) if gaps else np.inf), tau_gap
 
 
 def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = None) -> DecodeTrace:
@@ -195,13 +212,15 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
     arg = np.full(cfg.B, -1, np.int32)
     conf[masked] = head.conf.astype(np.float32)
     arg[masked] = head.arg
+    margin = np.full(cfg.B, np.inf)       # top-2 logit gap behind arg[p]
+    margin[masked] = head.margin
     tr = DecodeTrace(tok.copy(), conf.copy(), arg.copy(),
                      float(head.margin.min()) if head.margin.size else np.inf)
     limit = int(masked.size) if max_steps is None else max_steps
     for _ in range(limit):
         if not np.any(tok == MASK):
             break
-        rank_gap, tau_gap = _gaps(tok, conf, np.float64(np.float32(tau)))
+        rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k)
         # explore with the state, then the projections of every branch's tokens
         br = branch_build(tok, conf, arg, k, np.float32(tau), cfg.nb_max)
         st = block_inputs(inp, seed, br.br_tok.reshape(cfg.nb_max, cfg.B)[:br.nb])
@@ -210,10 +229,12 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
         bc = np.sort(np.asarray(sel.bconf[:out.br.nb], np.float64))[::-1]
         win_margin = float(bc[0] - bc[1]) if bc.size > 1 else np.inf
         new_tok = np.asarray(sel.tok_next, np.int32)
-        tr.steps.append(DecodeStep(out.br.nb, int(sel.winner), new_tok.copy(),
-                                   int(np.sum((tok == MASK) & (new_tok != MASK))),
-                                   float(out.head.margin.min()) if out.head.margin.size else np.inf,
+        filled = (tok == MASK) & (new_tok != MASK)
+        tr.steps.append(DecodeStep(out.br.nb, int(sel.winner), new_tok.copy(), int(filled.sum()),
+                                   float(margin[filled].min()) if filled.any() else np.inf,
                                    rank_gap, tau_gap, win_margin))
+        w = int(sel.winner)
+        margin = np.where(new_tok == MASK, out.margin_pos[w * cfg.B:(w + 1) * cfg.B], np.inf)
         tok = new_tok
         conf = np.asarray(sel.conf_next, np.float32)
         arg = np.asarray(sel.arg_next, np.int32)

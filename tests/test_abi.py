@@ -76,6 +76,8 @@ def test_null_pointers_and_k_rejected():
                               1 << 30, None) == -1
     assert L.lopa_branch_select(ctypes.byref(d), *([fake] * 9), None, None) == -1
     assert L.lopa_lmhead_conf(None, *([fake] * 8), fake, 1 << 30, None) == -1
+    assert L.lopa_synth_qkv(ctypes.byref(d), 1, None, fake, fake, fake, fake, None) == -1
+    assert L.lopa_synth_qkv(ctypes.byref(d), 1, fake, fake, fake, None, fake, None) == -1
 
 
 def test_workspace_size_and_shortfall():
