@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: prefix 512, k=4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the block-decoding measurement (steps per block, TPF)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the oracle's timed CPU work")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
@@ -79,6 +81,33 @@ def algorithmic(cfg, nb: int, M: int) -> dict:
     return dict(step_bytes=head_bytes + attn_bytes + small, head_bytes=head_bytes,
                 attn_bytes=attn_bytes, head_flops=head_flops, attn_flops=attn_flops,
                 w_bytes=w)
+
+
+def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10) -> dict:
+    """Decode the workload's block (its masked positions) from the initial
+    pass until none is masked, with token-keyed projections: steps, tokens per
+    step (TPF), and the time of the whole block (initial pass + its steps)."""
+    import torch
+    from lookahead_decoding_amd import MASK
+    from lookahead_decoding_amd.decode import DecodeBuffers, decode_block
+
+    m = int(np.sum(inp.tok == MASK))
+    buf = DecodeBuffers(dims)
+    log = torch.zeros(max(m, 1), cfg.B, dtype=torch.int32, device="cuda")
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log)
+    torch.cuda.synchronize()
+    got = log.cpu().numpy()
+    done = [s for s in range(m) if not np.any(got[s] == MASK)]
+    steps = done[0] + 1 if done else m
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    return {"k": k, "masked": m, "steps": steps, "tpf": round(m / steps, 3),
+            "ms_per_block": round(ms, 3), "decoded_tokens_per_s": round(m / (ms * 1e-3), 1)}
 
 
 def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
@@ -247,6 +276,14 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         out["copy_probe_bytes"] = a.numel() * a.element_size()
+    if not args.no_decode:
+        seed = 0x10FA + inp.seed
+        out["decode"] = {
+            "data": "token-keyed synthetic Q/K/V (Philox4x32-10, Irwin-Hall N(0,1)) and "
+                    "random weights: TPF shows the mechanism, not a trained model's rate",
+            "lookahead": decode_measure(dims, cfg, inp, x, cfg.k, seed),
+            "anchor_only": decode_measure(dims, cfg, inp, x, 0, seed),
+        }
     if not args.no_cpu_baseline:
         import oracle as O  # noqa: F401  (CPU baseline leg only)
         c, a, _ = O.initial_state(inp)
