@@ -201,6 +201,22 @@ int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
 int lopa_synth_qkv(const lopa_dims* dims, uint64_t seed, const int32_t* br_tok,
                    const int32_t* nb, void* Qb, void* Kb, void* Vb, hipStream_t stream);
 
+/*
+ * Commit of a decoded block: once a block is decoded, the winner's branch
+ * slot of Kb and Vb -- every slot holds its block's K and V from the last
+ * verification pass -- is appended to the committed prefix by index, not
+ * recomputed (the pre-write / commit-winner cache of the news article's
+ * section "系统级创新：LoPA-Dist 分布式推理"; the two-phase KV commit of
+ * "LoPA：上海交大與華為聯手破解AI推理新困境"), so the next block attends to it.
+ * Copies Kb[w], Vb[w] ([B][Hkv][d], w = *winner clamped to 0..nb_max-1) to
+ * rows at .. at+B-1 of Kp, Vp ([rows][Hkv][d]).
+ * In  winner[1] (e.g. as written by lopa_branch_select); Kb, Vb
+ *     [nb_max][B][Hkv][d]; at >= 0
+ * Out Kp, Vp rows at .. at+B-1; the caller's buffers must hold at+B rows.
+ */
+int lopa_commit_block(const lopa_dims* dims, const int32_t* winner, const void* Kb,
+                      const void* Vb, void* Kp, void* Vp, int32_t at, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

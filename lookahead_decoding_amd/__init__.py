@@ -71,6 +71,7 @@ _SIGS = {
                            ctypes.c_int),
     "lopa_synth_qkv": ([ctypes.POINTER(Dims), ctypes.c_uint64, _P, _P, _P, _P, _P, _P],
                        ctypes.c_int),
+    "lopa_commit_block": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _I, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -190,6 +191,14 @@ def lopa_synth_qkv(dims, seed, br_tok, nb, Qb, Kb, Vb, stream=None) -> None:
         ctypes.byref(dims), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(br_tok, i32, "br_tok"),
         _ptr(nb, i32, "nb"), _ptr(Qb, a, "Qb"), _ptr(Kb, a, "Kb"), _ptr(Vb, a, "Vb"),
         _stream(stream)))
+
+
+def lopa_commit_block(dims, winner, Kb, Vb, Kp, Vp, at, stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    _check("lopa_commit_block", lib().lopa_commit_block(
+        ctypes.byref(dims), _ptr(winner, torch.int32, "winner"), _ptr(Kb, a, "Kb"),
+        _ptr(Vb, a, "Vb"), _ptr(Kp, a, "Kp"), _ptr(Vp, a, "Vp"), int(at), _stream(stream)))
 
 
 from .step import StepBuffers, run_step, initial_pass  # noqa: E402,F401

@@ -119,3 +119,55 @@ extern "C" int lopa_synth_qkv(const lopa_dims* dims, uint64_t seed, const int32_
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Commit of a decoded block's K and V to the committed prefix.
+//
+// Every branch slot already holds its block's K and V (written for the last
+// verification pass); once the block is decoded, the winner's slot is kept by
+// index and appended to the prefix, not recomputed -- the pre-write and
+// commit-winner cache of the news article's section
+// "系统级创新：LoPA-Dist 分布式推理", in its one-GPU form.
+// ---------------------------------------------------------------------------
+
+namespace lopa {
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_commit_block(int n, int nb_max, const int32_t* __restrict__ winner, const T* __restrict__ Kb,
+               const T* __restrict__ Vb, T* __restrict__ Kp, T* __restrict__ Vp) {
+  const int w = min(max(*winner, 0), nb_max - 1);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const size_t src = static_cast<size_t>(w) * n + i;
+  Kp[i] = Kb[src];
+  Vp[i] = Vb[src];
+}
+
+}  // namespace lopa
+
+extern "C" int lopa_commit_block(const lopa_dims* dims, const int32_t* winner, const void* Kb,
+                                 const void* Vb, void* Kp, void* Vp, int32_t at,
+                                 hipStream_t stream) {
+  using namespace lopa;
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (!winner || !Kb || !Vb || !Kp || !Vp || at < 0) return LOPA_ERR_INVALID;
+  const int n = dims->B * dims->Hkv * dims->d;   // one slot of Kb / Vb
+  const size_t row0 = static_cast<size_t>(at) * dims->Hkv * dims->d;
+  const int nb_max = dims->k_max + 1;
+  const dim3 grid((n + 255) / 256);
+  if (dims->dtype == LOPA_F32) {
+    hipLaunchKernelGGL(k_commit_block<float>, grid, dim3(256), 0, stream, n, nb_max, winner,
+                       static_cast<const float*>(Kb), static_cast<const float*>(Vb),
+                       static_cast<float*>(Kp) + row0, static_cast<float*>(Vp) + row0);
+  } else {
+    hipLaunchKernelGGL(k_commit_block<unsigned short>, grid, dim3(256), 0, stream, n, nb_max,
+                       winner, static_cast<const unsigned short*>(Kb),
+                       static_cast<const unsigned short*>(Vb),
+                       static_cast<unsigned short*>(Kp) + row0,
+                       static_cast<unsigned short*>(Vp) + row0);
+  }
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}

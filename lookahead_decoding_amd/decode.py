@@ -92,3 +92,29 @@ def decode_block(dims, k, tau, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, steps:
         decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream)
         if log is not None:
             log[s].copy_(buf.tok)
+
+
+def decode_sequence(dims, k, tau, seed, blocks, Kp, Vp, W, buf: DecodeBuffers,
+                    logs=None, stream=None) -> int:
+    """Decode ``blocks`` (host int32 [B] arrays) one after another.  Kp and Vp
+    hold the committed prefix in their first dims.L rows and have room for
+    len(blocks) * B more; after block j is decoded (as many steps as it has
+    masked positions -- later steps change nothing) the winner's K and V slot
+    is appended at row L + j*B by lopa_commit_block, and block j+1 attends to
+    it.  ``buf`` must be sized for the longest prefix.  ``logs[j]`` (device
+    int32 [m_j][B]) receives block j's tokens after each step.  Returns the
+    final prefix length."""
+    from . import Dims, lopa_commit_block
+    import torch
+    L = dims.L
+    zero = torch.zeros(1, dtype=torch.int32, device=buf.tok.device)
+    for j, tok0 in enumerate(blocks):
+        dj = Dims(L=L, B=dims.B, Hq=dims.Hq, Hkv=dims.Hkv, d=dims.d, V=dims.V, k_max=dims.k_max,
+                  dtype=dims.dtype)
+        m = int(np.sum(np.asarray(tok0) == MASK))
+        decode_block(dj, k, tau, seed, tok0, Kp, Vp, W, buf, m,
+                     None if logs is None else logs[j], stream)
+        # with no step taken, slot 0 holds the block (written by the initial pass)
+        lopa_commit_block(dj, buf.winner if m else zero, buf.Kb, buf.Vb, Kp, Vp, L, stream)
+        L += dims.B
+    return L

@@ -29,7 +29,13 @@ Readings (where the pages are silent):
     number of verification passes after the initial one;
   * the state a block starts from comes from one pass of the initial tokens
     (branch slot 0 alone), as in ``lopa_oracle.initial_state``;
-  * TPF = tokens decoded in the block / steps.
+  * TPF = tokens decoded in the block / steps;
+  * several blocks: once a block is decoded, the K and V of its final tokens
+    -- the projections every branch slot already holds, so the winner's slot
+    is kept by index rather than recomputed ([news] section
+    "系统级创新：LoPA-Dist 分布式推理", its pre-write and commit-winner cache;
+    [pop] the two-phase KV commit) -- are appended to the committed prefix,
+    and the next block attends to the longer prefix.
 """
 from __future__ import annotations
 
@@ -239,3 +245,30 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
         conf = np.asarray(sel.conf_next, np.float32)
         arg = np.asarray(sel.arg_next, np.int32)
     return tr
+
+
+@dataclass
+class SequenceTrace:
+    blocks: list             # DecodeTrace per block
+    Kp: np.ndarray           # committed prefix after the last block [L0 + n*B][Hkv][d]
+    Vp: np.ndarray
+
+
+def decode_sequence(inp, seed: int, k: int, tau: float, blocks) -> SequenceTrace:
+    """Decode the blocks ``blocks`` (each an int32 [B] token array, MASK where
+    masked) one after another.  Block j attends to inp's prefix plus the
+    committed K, V of blocks 0..j-1: after a block is decoded, the K and V its
+    final tokens map to (``token_qkv``) are appended to the prefix."""
+    cfg = inp.cfg
+    Kp, Vp = inp.Kp, inp.Vp
+    traces = []
+    for tok0 in blocks:
+        cur = replace(inp, tok=np.asarray(tok0, np.int32), Kp=Kp, Vp=Vp,
+                      cfg=replace(cfg, L=Kp.shape[0]))
+        tr = decode_block(cur, seed, k, tau)
+        traces.append(tr)
+        final = tr.steps[-1].tok if tr.steps else np.asarray(tok0, np.int32)
+        _, K, V = token_qkv(seed, final[None, :], cfg.Hq, cfg.Hkv, cfg.d, inp.Qb.dtype)
+        Kp = np.concatenate([Kp, K[0]], axis=0)
+        Vp = np.concatenate([Vp, V[0]], axis=0)
+    return SequenceTrace(traces, Kp, Vp)

@@ -98,3 +98,58 @@ def test_gpu_decode_block(name, ov, k, tau, seed):
         assert np.all(got[n - 1:] == got[n - 1])
         if n > 1:
             assert np.any(got[n - 2] == O.MASK)
+
+
+def test_gpu_commit_block_copies_winner_slot():
+    from lookahead_decoding_amd import lopa_commit_block
+    dims = lopa.Dims(L=10, B=12, Hq=4, Hkv=2, d=64, V=64, k_max=3, dtype=lopa.BF16)
+    Kb = torch.randn(4, 12, 2, 64, device="cuda").to(torch.bfloat16)
+    Vb = torch.randn(4, 12, 2, 64, device="cuda").to(torch.bfloat16)
+    Kp = torch.zeros(10 + 24, 2, 64, dtype=torch.bfloat16, device="cuda")
+    Vp = torch.zeros_like(Kp)
+    for w, at in ((2, 10), (0, 22)):
+        lopa_commit_block(dims, to_device(np.array([w], np.int32)), Kb, Vb, Kp, Vp, at)
+    torch.cuda.synchronize()
+    assert torch.equal(Kp[10:22], Kb[2]) and torch.equal(Vp[10:22], Vb[2])
+    assert torch.equal(Kp[22:34], Kb[0]) and torch.equal(Vp[22:34], Vb[0])
+    assert torch.count_nonzero(Kp[:10]) == 0
+
+
+def test_gpu_decode_sequence_three_blocks():
+    from lookahead_decoding_amd.decode import decode_sequence
+    ov = dict(dtype="bf16", L=64, B=32, m=10, Hq=8, Hkv=2, d=128, V=4096, k=3)
+    inp = synth.make_inputs(synth.TINY, **ov)
+    cfg = inp.cfg
+    rng = np.random.default_rng(5)   # blocks whose decisions are clear-cut throughout
+    blocks = []
+    for m in (10, 14, 0):
+        tok = rng.integers(0, cfg.V, size=cfg.B).astype(np.int32)
+        tok[rng.choice(cfg.B, m, replace=False)] = O.MASK
+        blocks.append(tok)
+    seed, k, tau = 77, 3, 0.9
+    sq = D.decode_sequence(inp, seed, k, tau, blocks)
+    L0, B = cfg.L, cfg.B
+    dims_max = dims_of(cfg)
+    dims_max.L = L0 + 2 * B
+    buf = DecodeBuffers(dims_max)
+    Kp = torch.zeros(L0 + 3 * B, cfg.Hkv, cfg.d, dtype=torch.bfloat16, device="cuda")
+    Vp = torch.zeros_like(Kp)
+    Kp[:L0] = to_device(inp.Kp)
+    Vp[:L0] = to_device(inp.Vp)
+    W = to_device(inp.W)
+    logs = [torch.zeros(max(int(np.sum(b == O.MASK)), 1), B, dtype=torch.int32, device="cuda")
+            for b in blocks]
+    dims = dims_of(cfg)
+    L = decode_sequence(dims, k, tau, seed, blocks, Kp, Vp, W, buf, logs)
+    torch.cuda.synchronize()
+    assert L == L0 + 3 * B
+    for j, tr in enumerate(sq.blocks):
+        clear = all(st.fill_margin > TOK_MARGIN and st.rank_gap > GAP and st.tau_gap > GAP
+                    and st.win_margin > WIN for st in tr.steps)
+        assert clear, f"block {j} not clear-cut"
+        got = logs[j].cpu().numpy()
+        for s, st in enumerate(tr.steps):
+            assert np.array_equal(got[s], st.tok), f"block {j} step {s}"
+    # the committed prefix, bit for bit
+    g = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    assert np.array_equal(g(Kp), sq.Kp) and np.array_equal(g(Vp), sq.Vp)

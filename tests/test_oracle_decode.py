@@ -134,3 +134,36 @@ def test_decode_lookahead_never_slower_than_one_per_step():
     assert all(st.filled in (1, 2) for st in tr.steps)
     assert all((st.filled == 2) == (st.winner > 0) for st in tr.steps)
     assert tr.tpf >= 1.0
+
+
+def _blocks(B, n, m, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        tok = rng.integers(0, 500, size=B).astype(np.int32)
+        tok[rng.choice(B, m, replace=False)] = O.MASK
+        out.append(tok)
+    return out
+
+
+def test_sequence_appends_final_tokens_kv_and_later_blocks_see_it():
+    inp = _inp(L=24, B=16, m=8, k=3)
+    blocks = _blocks(16, 3, 6, 1)
+    sq = D.decode_sequence(inp, seed=5, k=3, tau=0.9, blocks=blocks)
+    L0, B = inp.Kp.shape[0], 16
+    assert sq.Kp.shape[0] == L0 + 3 * B and sq.Vp.shape == sq.Kp.shape
+    assert np.array_equal(sq.Kp[:L0], inp.Kp) and np.array_equal(sq.Vp[:L0], inp.Vp)
+    for j, tr in enumerate(sq.blocks):
+        final = tr.steps[-1].tok
+        assert not np.any(final == O.MASK)
+        _, K, V = D.token_qkv(5, final[None, :], inp.cfg.Hq, inp.cfg.Hkv, inp.cfg.d)
+        assert np.array_equal(sq.Kp[L0 + j * B:L0 + (j + 1) * B], K[0])
+        assert np.array_equal(sq.Vp[L0 + j * B:L0 + (j + 1) * B], V[0])
+    # block 1 decoded on the extended prefix, not on the original one
+    from dataclasses import replace
+    ext = replace(inp, tok=blocks[1], Kp=sq.Kp[:L0 + B], Vp=sq.Vp[:L0 + B],
+                  cfg=replace(inp.cfg, L=L0 + B))
+    again = D.decode_block(ext, 5, 3, 0.9)
+    assert np.array_equal(again.conf0, sq.blocks[1].conf0)
+    orig = D.decode_block(replace(inp, tok=blocks[1]), 5, 3, 0.9)
+    assert not np.array_equal(orig.conf0, sq.blocks[1].conf0)
