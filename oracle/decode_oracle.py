@@ -202,11 +202,14 @@ def _explore_gaps(tok, conf, tau, k):
     return (float(min(gaps)) if gaps else np.inf), tau_gap
 
 
-def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = None) -> DecodeTrace:
+def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = None,
+                 alpha: float | None = None) -> DecodeTrace:
     """Decode inp.tok's masked positions: the initial pass, then verification
     steps (explore, verify, select and reuse) until none is masked.  The
     committed prefix Kp, Vp and the weight W come from ``inp``; every
-    branch's Q, K, V come from ``token_qkv`` of that branch's tokens."""
+    branch's Q, K, V come from ``token_qkv`` of that branch's tokens.
+    ``alpha`` selects with the alternative branch score
+    (``lopa_oracle.branch_select_alpha``) instead of the mean confidence."""
     cfg = inp.cfg
     tok = np.asarray(inp.tok, np.int32).copy()
     # initial pass: branch slot 0 holds the block as it stands
@@ -230,7 +233,7 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
         # explore with the state, then the projections of every branch's tokens
         br = branch_build(tok, conf, arg, k, np.float32(tau), cfg.nb_max)
         st = block_inputs(inp, seed, br.br_tok.reshape(cfg.nb_max, cfg.B)[:br.nb])
-        out = verification_step(replace(st, tok=tok), conf, arg, k, tau)
+        out = verification_step(replace(st, tok=tok), conf, arg, k, tau, alpha)
         sel = out.sel
         bc = np.sort(np.asarray(sel.bconf[:out.br.nb], np.float64))[::-1]
         win_margin = float(bc[0] - bc[1]) if bc.size > 1 else np.inf

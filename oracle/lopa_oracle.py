@@ -270,18 +270,22 @@ class HeadOut:
     arg: np.ndarray       # [M] int64: argmax token (lowest id on a tie)
     margin: np.ndarray    # [M] float64: top-1 minus top-2 logit
     logits: np.ndarray | None = None   # [M][V] float64 when asked for
+    ent: np.ndarray | None = None      # [M] float64: entropy of softmax(l) / ln V
 
 
 def lmhead_conf(Hrows64: np.ndarray, W, keep_logits: bool = False) -> HeadOut:
     """Logits l = H_r . W_v for every row r and vocabulary entry v, in
-    float64; confidence = max_v softmax(l)_v; token = argmax_v l_v."""
+    float64; confidence = max_v softmax(l)_v; token = argmax_v l_v;
+    ent = -sum_v p_v ln p_v / ln V, the entropy of the position's
+    distribution normalised to [0, 1] (0 when V = 1) -- the H of the
+    alternative branch score of [blog] section 3.2."""
     W64 = to_f64(W)
     M = Hrows64.shape[0]
     V = W64.shape[0]
     if M == 0:
         e = np.zeros(0)
         return HeadOut(e, np.zeros(0, dtype=np.int64), e,
-                       np.zeros((0, V)) if keep_logits else None)
+                       np.zeros((0, V)) if keep_logits else None, e)
     logits = Hrows64 @ W64.T
     P = softmax_rows(logits)
     conf = P.max(axis=1)
@@ -291,7 +295,10 @@ def lmhead_conf(Hrows64: np.ndarray, W, keep_logits: bool = False) -> HeadOut:
         margin = top2[:, 1] - top2[:, 0]
     else:
         margin = np.full(M, np.inf)
-    return HeadOut(conf, arg, margin, logits if keep_logits else None)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(P > 0, P * np.log(P), 0.0)
+    ent = -plogp.sum(axis=1) / math.log(V) if V > 1 else np.zeros(M)
+    return HeadOut(conf, arg, margin, logits if keep_logits else None, ent)
 
 
 # ---------------------------------------------------------------------------
@@ -336,6 +343,39 @@ def branch_select(nb: int, br_mask, br_tok, conf_pos, arg_pos) -> Selection:
     return Selection(bconf, winner, margin, tok_next, conf_next, arg_next)
 
 
+def branch_select_alpha(nb: int, br_mask, br_tok, conf_pos, arg_pos, ent_pos, tok_state,
+                        conf_state, alpha: float) -> Selection:
+    """The alternative branch score of [blog] section 3.2:
+    score_b = alpha * sum of the probabilities of the tokens branch b fills
+    this step + (1 - alpha) * sum over the positions b leaves masked of
+    (1 - H), H the normalised entropy of the position's distribution in b's
+    verification pass.  Readings: the sums are taken as written (not
+    averaged); a fill's probability is the confidence it was filled on (the
+    state's); H is normalised by ln V so 1 - H lies in [0, 1].  Winner and
+    next state as in ``branch_select`` (the first best branch wins ties)."""
+    nb_max, B = br_mask.shape
+    score = np.full(nb_max, -1.0)
+    for b in range(nb):
+        fill = sum(float(conf_state[p]) for p in range(B)
+                   if tok_state[p] == MASK and not br_mask[b, p])
+        rest = sum(1.0 - float(ent_pos[b * B + p]) for p in range(B) if br_mask[b, p])
+        score[b] = alpha * fill + (1.0 - alpha) * rest
+    winner = 0
+    for b in range(1, nb):
+        if score[b] > score[winner]:
+            winner = b
+    others = [score[b] for b in range(nb) if b != winner]
+    margin = score[winner] - max(others) if others else math.inf
+    tok_next = br_tok[winner].astype(np.int32).copy()
+    conf_next = np.zeros(B)
+    arg_next = np.full(B, -1, dtype=np.int32)
+    for p in range(B):
+        if br_mask[winner, p]:
+            conf_next[p] = float(conf_pos[winner * B + p])
+            arg_next[p] = int(arg_pos[winner * B + p])
+    return Selection(score, winner, margin, tok_next, conf_next, arg_next)
+
+
 # ---------------------------------------------------------------------------
 # Whole step and the pass that produces the state a step starts from
 # ---------------------------------------------------------------------------
@@ -349,6 +389,7 @@ class StepOut:
     arg_pos: np.ndarray    # [nb_max*B] int64 (-1 where not listed)
     margin_pos: np.ndarray  # [nb_max*B] float64 (inf where not listed)
     sel: Selection
+    ent_pos: np.ndarray | None = None   # [nb_max*B] float64 (0 where not listed)
 
 
 def initial_state(inp) -> tuple[np.ndarray, np.ndarray, HeadOut]:
@@ -370,10 +411,11 @@ def initial_state(inp) -> tuple[np.ndarray, np.ndarray, HeadOut]:
 
 
 def verification_step(inp, conf, arg, k: int | None = None,
-                      tau: float | None = None) -> StepOut:
+                      tau: float | None = None, alpha: float | None = None) -> StepOut:
     """One LoPA iteration: explore, verify (attention + LM head) and select.
 
-    ``conf`` must be float32 (the library's input precision)."""
+    ``conf`` must be float32 (the library's input precision).  ``alpha``
+    selects with ``branch_select_alpha`` instead of the mean confidence."""
     cfg = inp.cfg
     k = cfg.k if k is None else k
     tau = cfg.tau if tau is None else tau
@@ -387,9 +429,15 @@ def verification_step(inp, conf, arg, k: int | None = None,
     conf_pos = np.zeros(n)
     arg_pos = np.full(n, -1, dtype=np.int64)
     margin_pos = np.full(n, np.inf)
+    ent_pos = np.zeros(n)
     for i, r in enumerate(br.rows):
         conf_pos[r] = head.conf[i]
         arg_pos[r] = head.arg[i]
         margin_pos[r] = head.margin[i]
-    sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
-    return StepOut(br, H, head, conf_pos, arg_pos, margin_pos, sel)
+        ent_pos[r] = head.ent[i]
+    if alpha is None:
+        sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
+    else:
+        sel = branch_select_alpha(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos, ent_pos,
+                                  inp.tok, conf, alpha)
+    return StepOut(br, H, head, conf_pos, arg_pos, margin_pos, sel, ent_pos)
