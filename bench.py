@@ -83,10 +83,11 @@ def algorithmic(cfg, nb: int, M: int) -> dict:
                 w_bytes=w)
 
 
-def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10) -> dict:
+def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10, alpha=None) -> dict:
     """Decode the workload's block (its masked positions) from the initial
     pass until none is masked, with token-keyed projections: steps, tokens per
-    step (TPF), and the time of the whole block (initial pass + its steps)."""
+    step (TPF), and the time of the whole block (initial pass + its steps).
+    ``alpha``: select with the entropy-weighted branch score instead."""
     import torch
     from lookahead_decoding_amd import MASK
     from lookahead_decoding_amd.decode import DecodeBuffers, decode_block
@@ -94,19 +95,22 @@ def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10) -> dict
     m = int(np.sum(inp.tok == MASK))
     buf = DecodeBuffers(dims)
     log = torch.zeros(max(m, 1), cfg.B, dtype=torch.int32, device="cuda")
-    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log)
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log,
+                 alpha=alpha)
     torch.cuda.synchronize()
     got = log.cpu().numpy()
     done = [s for s in range(m) if not np.any(got[s] == MASK)]
     steps = done[0] + 1 if done else m
-    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps)
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps,
+                 alpha=alpha)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
-        decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps)
+        decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps,
+                     alpha=alpha)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / reps * 1e3
-    return {"k": k, "masked": m, "steps": steps, "tpf": round(m / steps, 3),
+    return {"k": k, "alpha": alpha, "masked": m, "steps": steps, "tpf": round(m / steps, 3),
             "ms_per_block": round(ms, 3), "decoded_tokens_per_s": round(m / (ms * 1e-3), 1)}
 
 
@@ -227,6 +231,21 @@ def main():
     torch.cuda.synchronize()
     per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
     call_us = per.mean(axis=0) * 1e3
+    # the entropy-carrying LM head and the alternative select on the same rows
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        e = ev2[i]
+        e[0].record(stream)
+        lopa.lopa_lmhead_conf_ent(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
+                                  buf.arg, buf.ent, None, buf.ws)
+        e[1].record(stream)
+        lopa.lopa_branch_select_alpha(dims, 0.5, x["tok"], x["conf"], buf.nb, buf.br_mask,
+                                      buf.br_tok, buf.conf, buf.arg, buf.ent, buf.bconf,
+                                      buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    alt_us = np.array([[ev2[i][j].elapsed_time(ev2[i][j + 1]) for j in range(2)]
+                       for i in range(K)]).mean(axis=0) * 1e3
     # the roofline uses the LM-head call timed inside the timed loop (eager), else the
     # separate per-call loop (graph replay has no per-call events)
     head_us = head_timed_us if head_timed_us is not None else float(call_us[2])
@@ -260,7 +279,9 @@ def main():
         "call_us": {"branch_build": round(float(call_us[0]), 2),
                     "branch_attn": round(float(call_us[1]), 2),
                     "lmhead_conf": round(float(call_us[2]), 2),
-                    "branch_select": round(float(call_us[3]), 2)},
+                    "branch_select": round(float(call_us[3]), 2),
+                    "lmhead_conf_ent": round(float(alt_us[0]), 2),
+                    "branch_select_alpha": round(float(alt_us[1]), 2)},
         "roofline": {"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -283,6 +304,7 @@ def main():
                     "random weights: TPF shows the mechanism, not a trained model's rate",
             "lookahead": decode_measure(dims, cfg, inp, x, cfg.k, seed),
             "anchor_only": decode_measure(dims, cfg, inp, x, 0, seed),
+            "lookahead_alpha_0.5": decode_measure(dims, cfg, inp, x, cfg.k, seed, alpha=0.5),
         }
     if not args.no_cpu_baseline:
         import oracle as O  # noqa: F401  (CPU baseline leg only)

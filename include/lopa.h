@@ -163,6 +163,23 @@ int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
                      hipStream_t stream);
 
 /*
+ * lopa_lmhead_conf plus, for every listed row, the normalised entropy of the
+ * row's softmax distribution:
+ *   ent[r] = -(sum_v p_v ln p_v) / ln V,  p = softmax(l)   (0 when V == 1)
+ * gathered in the same streaming pass (each partial also carries
+ * t = sum exp(l - max) (l - max); entropy = ln s - t / s).  The input to the
+ * alternative branch score of lopa_branch_select_alpha.
+ * ["解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈", section 3.2]
+ * Out ent[nb_max*B] float -- only listed entries written (non-NULL, else
+ *     LOPA_ERR_INVALID); everything else as lopa_lmhead_conf.
+ */
+int lopa_lmhead_conf_ent(const lopa_dims* dims, const void* H, const void* W,
+                         const int32_t* rows, const int32_t* row_ptr,
+                         const int32_t* nb, float* conf, int32_t* arg, float* ent,
+                         float* logits_out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
  * Select and reuse: branch confidence bconf[b] = mean of conf[b*B+p] over
  * the p with br_mask[b*B+p] = 1 (1.0 when there is none), for b < nb;
  * bconf[b] = -1 for b >= nb.  winner = the first b with the largest bconf
@@ -177,6 +194,31 @@ int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
                        const float* conf, const int32_t* arg,
                        float* bconf, int32_t* winner, int32_t* tok_next,
                        float* conf_next, int32_t* arg_next, hipStream_t stream);
+
+/*
+ * Select and reuse with the alternative branch score of
+ * ["解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈", section 3.2], which weighs
+ * the confidence of what a branch fills now against the certainty it leaves
+ * for the positions still masked:
+ *   score[b] = alpha * sum of conf_state[p] over the p that branch b fills
+ *              (tok[p] == LOPA_MASK_TOKEN, br_mask[b*B+p] == 0)
+ *            + (1 - alpha) * sum of (1 - ent[b*B+p]) over the p with
+ *              br_mask[b*B+p] == 1
+ * for b < nb; score[b] = -1 for b >= nb.  The sums are taken as written (not
+ * averaged); the probability of a filled token is the confidence it was
+ * filled on.  Winner and next state as in lopa_branch_select.
+ * In  alpha in [0, 1] (else LOPA_ERR_INVALID); tok[B], conf_state[B]: the
+ *     state the step started from (the arrays given to lopa_branch_build);
+ *     nb, br_mask, br_tok, conf, arg, ent (lopa_lmhead_conf_ent)
+ * Out score[nb_max] float, winner[1], tok_next[B], conf_next[B], arg_next[B].
+ *     float32 sums; one wavefront.
+ */
+int lopa_branch_select_alpha(const lopa_dims* dims, float alpha, const int32_t* tok,
+                             const float* conf_state, const int32_t* nb,
+                             const uint8_t* br_mask, const int32_t* br_tok,
+                             const float* conf, const int32_t* arg, const float* ent,
+                             float* score, int32_t* winner, int32_t* tok_next,
+                             float* conf_next, int32_t* arg_next, hipStream_t stream);
 
 /*
  * Token-keyed synthetic projections, for decoding a whole block over several

@@ -69,6 +69,10 @@ _SIGS = {
                          ctypes.c_int),
     "lopa_branch_select": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                            ctypes.c_int),
+    "lopa_lmhead_conf_ent": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              ctypes.c_size_t, _P], ctypes.c_int),
+    "lopa_branch_select_alpha": ([ctypes.POINTER(Dims), ctypes.c_float] + [_P] * 14,
+                                 ctypes.c_int),
     "lopa_synth_qkv": ([ctypes.POINTER(Dims), ctypes.c_uint64, _P, _P, _P, _P, _P, _P],
                        ctypes.c_int),
     "lopa_commit_block": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _I, _P], ctypes.c_int),
@@ -180,6 +184,34 @@ def lopa_branch_select(dims, nb, br_mask, br_tok, conf, arg, bconf, winner, tok_
         ctypes.byref(dims), _ptr(nb, i32, "nb"), _ptr(br_mask, torch.uint8, "br_mask"),
         _ptr(br_tok, i32, "br_tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
         _ptr(bconf, f32, "bconf"), _ptr(winner, i32, "winner"), _ptr(tok_next, i32, "tok_next"),
+        _ptr(conf_next, f32, "conf_next"), _ptr(arg_next, i32, "arg_next"), _stream(stream)))
+
+
+def lopa_lmhead_conf_ent(dims, H, W, rows, row_ptr, nb, conf, arg, ent, logits_out, ws,
+                         stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    i32, f32 = torch.int32, torch.float32
+    if ent is None:
+        raise ValueError("ent is required")
+    _check("lopa_lmhead_conf_ent", lib().lopa_lmhead_conf_ent(
+        ctypes.byref(dims), _ptr(H, a, "H"), _ptr(W, a, "W"), _ptr(rows, i32, "rows"),
+        _ptr(row_ptr, i32, "row_ptr"), _ptr(nb, i32, "nb"), _ptr(conf, f32, "conf"),
+        _ptr(arg, i32, "arg"), _ptr(ent, f32, "ent"), _ptr(logits_out, f32, "logits_out"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def lopa_branch_select_alpha(dims, alpha, tok, conf_state, nb, br_mask, br_tok, conf, arg, ent,
+                             score, winner, tok_next, conf_next, arg_next, stream=None) -> None:
+    import torch
+    i32, f32 = torch.int32, torch.float32
+    _check("lopa_branch_select_alpha", lib().lopa_branch_select_alpha(
+        ctypes.byref(dims), float(alpha), _ptr(tok, i32, "tok"),
+        _ptr(conf_state, f32, "conf_state"), _ptr(nb, i32, "nb"),
+        _ptr(br_mask, torch.uint8, "br_mask"), _ptr(br_tok, i32, "br_tok"),
+        _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"), _ptr(ent, f32, "ent"),
+        _ptr(score, f32, "score"), _ptr(winner, i32, "winner"), _ptr(tok_next, i32, "tok_next"),
         _ptr(conf_next, f32, "conf_next"), _ptr(arg_next, i32, "arg_next"), _stream(stream)))
 
 

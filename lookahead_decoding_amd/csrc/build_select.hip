@@ -83,10 +83,16 @@ k_branch_build(int B, int nb_max, int k, float tau,
   }
 }
 
+// ALPHA: the alternative branch score (alpha * the state confidences of the
+// positions branch b fills + (1 - alpha) * the sum of 1 - ent over the
+// positions it leaves masked) in place of the mean confidence.
+template <bool ALPHA>
 __global__ void __launch_bounds__(64)
 k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
                 const uint8_t* __restrict__ br_mask, const int32_t* __restrict__ br_tok,
                 const float* __restrict__ conf, const int32_t* __restrict__ arg,
+                float alpha, const int32_t* __restrict__ tok_state,
+                const float* __restrict__ conf_state, const float* __restrict__ ent,
                 float* __restrict__ bconf, int32_t* __restrict__ winner,
                 int32_t* __restrict__ tok_next, float* __restrict__ conf_next,
                 int32_t* __restrict__ arg_next) {
@@ -94,6 +100,12 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
   const bool live = p < B;
   const int pc = live ? p : B - 1;   // in-bounds index for idle lanes
   const int nb = *nb_ptr;
+  bool was_masked = false;
+  float cs = 0.f;
+  if constexpr (ALPHA) {
+    was_masked = live && tok_state[pc] == LOPA_MASK_TOKEN;
+    cs = conf_state[pc];
+  }
   // every slot's flag and confidence is fetched before any is used
   uint8_t mk[LOPA_MAX_BRANCHES];
   float cf[LOPA_MAX_BRANCHES];
@@ -113,7 +125,14 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
 #pragma unroll
   for (int b = 0; b < LOPA_MAX_BRANCHES; ++b) {
     const bool m = live && mk[b] != 0;
-    sm[b] = m ? cf[b] : 0.f;
+    if constexpr (ALPHA) {
+      const int bb = b < nb_max ? b : nb_max - 1;
+      const float keep = m ? 1.f - ent[bb * B + pc] : 0.f;
+      const float fill = was_masked && !m ? cs : 0.f;
+      sm[b] = alpha * fill + (1.f - alpha) * keep;
+    } else {
+      sm[b] = m ? cf[b] : 0.f;
+    }
     cnt[b] = __popcll(__ballot(m));
   }
 #pragma unroll
@@ -131,7 +150,8 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
     if (b >= nb_max) break;
     float bc = -1.f;
     if (b < nb) {
-      bc = cnt[b] ? sm[b] / static_cast<float>(cnt[b]) : 1.f;
+      if constexpr (ALPHA) bc = sm[b];
+      else bc = cnt[b] ? sm[b] / static_cast<float>(cnt[b]) : 1.f;
       if (b == 0 || bc > best) {
         best = bc;
         w = b;
@@ -187,9 +207,29 @@ extern "C" int lopa_branch_select(const lopa_dims* dims, const int32_t* nb,
   if (!nb || !br_mask || !br_tok || !conf || !arg || !bconf || !winner || !tok_next ||
       !conf_next || !arg_next)
     return LOPA_ERR_INVALID;
-  hipLaunchKernelGGL(lopa::k_branch_select, dim3(1), dim3(64), 0, stream, dims->B,
-                     dims->k_max + 1, nb, br_mask, br_tok, conf, arg, bconf, winner,
-                     tok_next, conf_next, arg_next);
+  hipLaunchKernelGGL(lopa::k_branch_select<false>, dim3(1), dim3(64), 0, stream, dims->B,
+                     dims->k_max + 1, nb, br_mask, br_tok, conf, arg, 0.f, nullptr, nullptr,
+                     nullptr, bconf, winner, tok_next, conf_next, arg_next);
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}
+
+extern "C" int lopa_branch_select_alpha(const lopa_dims* dims, float alpha,
+                                        const int32_t* tok, const float* conf_state,
+                                        const int32_t* nb, const uint8_t* br_mask,
+                                        const int32_t* br_tok, const float* conf,
+                                        const int32_t* arg, const float* ent, float* score,
+                                        int32_t* winner, int32_t* tok_next, float* conf_next,
+                                        int32_t* arg_next, hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (!(alpha >= 0.f && alpha <= 1.f)) return LOPA_ERR_INVALID;
+  if (!tok || !conf_state || !nb || !br_mask || !br_tok || !conf || !arg || !ent || !score ||
+      !winner || !tok_next || !conf_next || !arg_next)
+    return LOPA_ERR_INVALID;
+  hipLaunchKernelGGL(lopa::k_branch_select<true>, dim3(1), dim3(64), 0, stream, dims->B,
+                     dims->k_max + 1, nb, br_mask, br_tok, conf, arg, alpha, tok, conf_state, ent,
+                     score, winner, tok_next, conf_next, arg_next);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;
 }

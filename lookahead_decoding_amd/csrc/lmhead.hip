@@ -47,8 +47,8 @@ __device__ __forceinline__ int swz(int r, int s) {
 // Online-softmax partial of one lane's logits for one LM-head row:
 // a[n][r] = logit of vocabulary entry vb + 32n + 8(r/4) + 4h + r%4 (the
 // 32x32 MFMA output layout, h = lane / 32), merged with the other lane half
-// that holds the same row.
-template <int NV>
+// that holds the same row.  ENT: also the entropy term t (else t = 0).
+template <int NV, bool ENT>
 __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, int h, int vend) {
   Partial p = empty_partial();
 #pragma unroll
@@ -62,15 +62,21 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
       }
     }
   if (p.i != 0x7fffffff) {
-    float s = 0.f;
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = vb + n * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (v < vend) s += exp2f((a[n][r] - p.m) * kLog2e);
+        if (v < vend) {
+          const float dl = a[n][r] - p.m;
+          const float e = exp2f(dl * kLog2e);
+          s += e;
+          if constexpr (ENT) t = fmaf(e, dl, t);
+        }
       }
     p.s = s;
+    p.t = t;
   }
   return merge(p, shfl_xor(p, 32));
 }
@@ -102,7 +108,7 @@ struct HeadTile {
   static_assert(HROWS <= RUNS, "running partials");
 };
 constexpr int kHeadStage = (256 + 128) * kRB;        // largest BUF of the bodies below
-constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * 12;
+constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(sizeof(Partial));
 
 // s_waitcnt on the vector-memory counter only (lgkm and exp counts left open).
 template <int N>
@@ -134,14 +140,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the workgroup's range, so loads past it return zeros without touching
 // memory.  Chunks are visited in an order rotated by the part, so the
 // compute units of one XCD do not all ask for the same H lines at once.
-template <int WX, int NVW, int MTW>
+template <int WX, int NVW, int MTW, bool ENT>
 __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int part, int Mg,
                                           int row0, int h_bytes,
                                           const unsigned short* __restrict__ H,
                                           const unsigned short* __restrict__ W,
                                           const int32_t* __restrict__ rows, unsigned char* smem,
                                           float* __restrict__ ws_m, float* __restrict__ ws_s,
-                                          int32_t* __restrict__ ws_i,
+                                          int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
                                           float* __restrict__ logits_out) {
   using T = HeadTile<WX, NVW, MTW>;
   constexpr int WROWS = T::WROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
@@ -256,9 +262,13 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
       const int vbw = v_lo + pass * WROWS + wx * (32 * NVW);
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
-        const Partial p = row_partial<NVW>(acc[mt], vbw, lh, v_hi);
+        const Partial p = row_partial<NVW, ENT>(acc[mt], vbw, lh, v_hi);
         const int r = (wy * MTW + mt) * 32 + ln;
-        if (lh == 0) run[wx * T::RUNS + r] = merge(run[wx * T::RUNS + r], p);
+        if (lh == 0) {
+          Partial q = merge(run[wx * T::RUNS + r], p);
+          if constexpr (!ENT) q.t = 0.f;   // keeps the entropy arithmetic out
+          run[wx * T::RUNS + r] = q;
+        }
         if (logits_out && r < Mg) {
           const size_t lb = static_cast<size_t>(rows[row0 + r]) * V;
 #pragma unroll
@@ -288,6 +298,7 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     ws_m[o] = p.m;
     ws_s[o] = p.s;
     ws_i[o] = p.i;
+    if constexpr (ENT) ws_t[o] = p.t;
   }
 }
 
@@ -295,12 +306,14 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
 // on XCD b % 8; the row groups of one vocabulary part take consecutive
 // blocks of the same XCD, so they stream the same weight lines together and
 // the second reader is served from that XCD's L2 (or the MALL behind it).
+// ENT: the partials also carry the entropy term.
+template <bool ENT>
 __global__ void __launch_bounds__(kHeadThreads)
 k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
               const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
-              float* __restrict__ ws_s, int32_t* __restrict__ ws_i,
+              float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
               float* __restrict__ logits_out) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHeadSmem];
   const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
@@ -314,14 +327,14 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
   if (part >= g.nparts || row0 >= M) return;
   const int Mg = min(M - row0, g.tpg * 32);
 #define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
-                  logits_out
+                  ws_t, logits_out
   // up to 4 tiles: 4 x 2 compute waves (256 vocabulary rows per pass);
   // 5..8 tiles: 2 x 4 compute waves (128 vocabulary rows per pass)
   if (!g.wide) {
-    if (g.tpg <= 2) head_body<4, 2, 1>(LOPA_ARGS);
-    else head_body<4, 2, 2>(LOPA_ARGS);
+    if (g.tpg <= 2) head_body<4, 2, 1, ENT>(LOPA_ARGS);
+    else head_body<4, 2, 2, ENT>(LOPA_ARGS);
   } else {
-    head_body<2, 2, 2>(LOPA_ARGS);
+    head_body<2, 2, 2, ENT>(LOPA_ARGS);
   }
 #undef LOPA_ARGS
 }
@@ -336,7 +349,7 @@ k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __
                const T* __restrict__ W,
                const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
                const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
-               float* __restrict__ ws_s, int32_t* __restrict__ ws_i,
+               float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
                float* __restrict__ logits_out) {
   __shared__ Partial red[4];
   const int m = blockIdx.y;
@@ -350,7 +363,7 @@ k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __
     const size_t hb = static_cast<size_t>(row) * hidden;
     const size_t wb = static_cast<size_t>(v) * hidden;
     for (int k = 0; k < hidden; ++k) l = fmaf(Act<T>::load(H, hb + k), Act<T>::load(W, wb + k), l);
-    p = Partial{l, 1.f, v};
+    p = Partial{l, 1.f, v, 0.f};
     if (logits_out) logits_out[static_cast<size_t>(row) * V + v] = l;
   }
 #pragma unroll
@@ -363,19 +376,23 @@ k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __
     ws_m[o] = p.m;
     ws_s[o] = p.s;
     ws_i[o] = p.i;
+    if (ws_t) ws_t[o] = p.t;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the vocabulary tiles of each row: conf = 1 / sum, arg = argmax.
+// Merge of the vocabulary tiles of each row: conf = 1 / sum, arg = argmax,
+// and where ent is given the entropy of the row's softmax divided by ln V
+// (0 when V == 1).
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256)
-k_lmhead_merge(int ntiles, int mfma, int nb_max, int m_max,
+k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
                const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
                const int32_t* __restrict__ nb_ptr, const float* __restrict__ ws_m,
                const float* __restrict__ ws_s, const int32_t* __restrict__ ws_i,
-               float* __restrict__ conf, int32_t* __restrict__ arg) {
+               const float* __restrict__ ws_t, float* __restrict__ conf,
+               int32_t* __restrict__ arg, float* __restrict__ ent) {
   __shared__ Partial red[4];
   const int m = blockIdx.x;
   const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
@@ -384,7 +401,8 @@ k_lmhead_merge(int ntiles, int mfma, int nb_max, int m_max,
   Partial p = empty_partial();
   const size_t base = static_cast<size_t>(m) * ntiles;
   for (int t = threadIdx.x; t < ntiles; t += 256)
-    p = merge(p, Partial{ws_m[base + t], ws_s[base + t], ws_i[base + t]});
+    p = merge(p, Partial{ws_m[base + t], ws_s[base + t], ws_i[base + t],
+                         ent ? ws_t[base + t] : 0.f});
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) p = merge(p, shfl_xor(p, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
@@ -394,16 +412,17 @@ k_lmhead_merge(int ntiles, int mfma, int nb_max, int m_max,
     const int r = rows[m];
     conf[r] = 1.f / p.s;
     arg[r] = p.i;
+    if (ent) ent[r] = V > 1 ? (logf(p.s) - p.t / p.s) / logf(static_cast<float>(V)) : 0.f;
   }
 }
 
 }  // namespace lopa
 
-extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
-                                const int32_t* rows, const int32_t* row_ptr,
-                                const int32_t* nb, float* conf, int32_t* arg,
-                                float* logits_out, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+// Both entry points: ent == nullptr leaves the entropy out.
+static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
+                         const int32_t* rows, const int32_t* row_ptr, const int32_t* nb,
+                         float* conf, int32_t* arg, float* ent, float* logits_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   using namespace lopa;
   int st = lopa_check_dims(dims);
   if (st != LOPA_OK) return st;
@@ -416,31 +435,57 @@ extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void
   float* wm = static_cast<float*>(ws);
   float* wsum = wm + plane;
   int32_t* wi = reinterpret_cast<int32_t*>(wsum + plane);
+  float* wt = ent ? reinterpret_cast<float*>(wi + plane) : nullptr;
   const int V = dims->V;
   const int nb_max = dims->k_max + 1;
   const unsigned short* Hb = static_cast<const unsigned short*>(H);
   const unsigned short* Wb = static_cast<const unsigned short*>(W);
   const int h_bytes = p.m_max * hidden * 2;   // H is [nb_max][B][hidden]
   if (p.mfma) {
-    hipLaunchKernelGGL(k_lmhead_mfma, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V, hidden, nb_max,
-                       p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi, logits_out);
+    if (ent)
+      hipLaunchKernelGGL(k_lmhead_mfma<true>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V,
+                         hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum,
+                         wi, wt, logits_out);
+    else
+      hipLaunchKernelGGL(k_lmhead_mfma<false>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream,
+                         V, hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum,
+                         wi, wt, logits_out);
   } else {
     const dim3 grid(p.ntiles, p.m_max);
     if (dims->dtype == LOPA_F32) {
       hipLaunchKernelGGL(k_lmhead_plain<float>, grid, dim3(256), 0, stream, V, hidden, p.ntiles,
                          nb_max, p.m_max, static_cast<const float*>(H),
-                         static_cast<const float*>(W), rows, row_ptr, nb, wm, wsum, wi,
+                         static_cast<const float*>(W), rows, row_ptr, nb, wm, wsum, wi, wt,
                          logits_out);
     } else {
       hipLaunchKernelGGL(k_lmhead_plain<unsigned short>, grid, dim3(256), 0, stream, V, hidden,
-                         p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi,
+                         p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi, wt,
                          logits_out);
     }
   }
   LOPA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_lmhead_merge, dim3(p.m_max), dim3(256), 0, stream, p.ntiles,
-                     p.mfma ? 1 : 0, nb_max, p.m_max, rows,
-                     row_ptr, nb, wm, wsum, wi, conf, arg);
+  hipLaunchKernelGGL(k_lmhead_merge, dim3(p.m_max), dim3(256), 0, stream, V, p.ntiles,
+                     p.mfma ? 1 : 0, nb_max, p.m_max, rows, row_ptr, nb, wm, wsum, wi, wt, conf,
+                     arg, ent);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;
+}
+
+extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
+                                const int32_t* rows, const int32_t* row_ptr,
+                                const int32_t* nb, float* conf, int32_t* arg,
+                                float* logits_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return lmhead_launch(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr, logits_out, ws,
+                       ws_bytes, stream);
+}
+
+extern "C" int lopa_lmhead_conf_ent(const lopa_dims* dims, const void* H, const void* W,
+                                    const int32_t* rows, const int32_t* row_ptr,
+                                    const int32_t* nb, float* conf, int32_t* arg, float* ent,
+                                    float* logits_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!ent) return LOPA_ERR_INVALID;
+  return lmhead_launch(dims, H, W, rows, row_ptr, nb, conf, arg, ent, logits_out, ws, ws_bytes,
+                       stream);
 }

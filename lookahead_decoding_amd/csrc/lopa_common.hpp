@@ -66,17 +66,23 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 }
 
 // Online-softmax partial over a set of logits l: m = max l, s = sum
-// exp(l - m), i = lowest index attaining m.  The empty partial has s == 0.
+// exp(l - m), i = lowest index attaining m, t = sum exp(l - m) (l - m) (the
+// entropy of softmax(l) is ln s - t / s).  The empty partial has s == 0.
 struct Partial {
   float m;
   float s;
   int i;
+  float t;
 };
 
-__device__ __forceinline__ Partial empty_partial() { return Partial{-INFINITY, 0.f, 0x7fffffff}; }
+__device__ __forceinline__ Partial empty_partial() {
+  return Partial{-INFINITY, 0.f, 0x7fffffff, 0.f};
+}
 
 // Merge of two partials over disjoint index sets; exact in (m, i), and the
-// sums are rescaled to the larger max.
+// sums are rescaled to the larger max: with c = exp(m' - M),
+// e^(l - M) = c e^(l - m') and (l - M) = (l - m') + (m' - M), so
+// t -> c (t + (m' - M) s).
 __device__ __forceinline__ Partial merge(Partial a, Partial b) {
   if (b.s == 0.f) return a;
   if (a.s == 0.f) return b;
@@ -88,7 +94,10 @@ __device__ __forceinline__ Partial merge(Partial a, Partial b) {
     r.m = a.m;
     r.i = a.i;
   }
-  r.s = a.s * exp2f((a.m - r.m) * kLog2e) + b.s * exp2f((b.m - r.m) * kLog2e);
+  const float da = a.m - r.m, db = b.m - r.m;
+  const float ca = exp2f(da * kLog2e), cb = exp2f(db * kLog2e);
+  r.s = a.s * ca + b.s * cb;
+  r.t = ca * fmaf(da, a.s, a.t) + cb * fmaf(db, b.s, b.t);
   return r;
 }
 
@@ -107,6 +116,7 @@ __device__ __forceinline__ Partial shfl_xor(Partial p, int o) {
   q.m = __shfl_xor(p.m, o, kWave);
   q.s = __shfl_xor(p.s, o, kWave);
   q.i = __shfl_xor(p.i, o, kWave);
+  q.t = __shfl_xor(p.t, o, kWave);
   return q;
 }
 

@@ -10,13 +10,19 @@ branch) -> lopa_branch_attn -> lopa_lmhead_conf -> lopa_branch_select, with the
 state (tokens, confidence, argmax) ping-ponged between two device buffers and
 never read back by the host.  A step taken after the block is complete
 changes nothing (no position is masked, so nothing is filled).
+
+With ``alpha`` given, the LM head also returns each row's normalised entropy
+(lopa_lmhead_conf_ent) and the winner is chosen by the alternative branch
+score of "解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈", section 3.2
+(lopa_branch_select_alpha).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_select,
-               lopa_lmhead_conf, lopa_synth_qkv)
+               lopa_branch_select_alpha, lopa_lmhead_conf, lopa_lmhead_conf_ent,
+               lopa_synth_qkv)
 from .step import StepBuffers
 
 
@@ -69,27 +75,35 @@ def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None) ->
     buf.arg_s.copy_(buf.arg[:B])
 
 
-def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None) -> None:
+def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
+                alpha=None) -> None:
     """One explore / verify / select step on the current state, then swap in
     the winner's state."""
     lopa_branch_build(dims, k, tau, buf.tok, buf.conf_s, buf.arg_s, buf.nb, buf.br_tok,
                       buf.br_mask, buf.rows, buf.row_ptr, stream)
     lopa_synth_qkv(dims, seed, buf.br_tok, buf.nb, buf.Qb, buf.Kb, buf.Vb, stream)
     lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.nb, buf.H, buf.ws, stream)
-    lopa_lmhead_conf(dims, buf.H, W, buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg, None,
-                     buf.ws, stream)
-    lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
-                       buf.winner, buf.tok_next, buf.conf_next, buf.arg_next, stream)
+    if alpha is None:
+        lopa_lmhead_conf(dims, buf.H, W, buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg, None,
+                         buf.ws, stream)
+        lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
+                           buf.winner, buf.tok_next, buf.conf_next, buf.arg_next, stream)
+    else:
+        lopa_lmhead_conf_ent(dims, buf.H, W, buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg,
+                             buf.ent, None, buf.ws, stream)
+        lopa_branch_select_alpha(dims, alpha, buf.tok, buf.conf_s, buf.nb, buf.br_mask,
+                                 buf.br_tok, buf.conf, buf.arg, buf.ent, buf.bconf, buf.winner,
+                                 buf.tok_next, buf.conf_next, buf.arg_next, stream)
     buf.swap_state()
 
 
 def decode_block(dims, k, tau, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, steps: int,
-                 log=None, stream=None) -> None:
+                 log=None, stream=None, alpha=None) -> None:
     """The initial pass and ``steps`` steps; ``log`` (device int32
     [steps][B]) receives the tokens after each step."""
     start_block(dims, seed, tok0, Kp, Vp, W, buf, stream)
     for s in range(steps):
-        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream)
+        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream, alpha)
         if log is not None:
             log[s].copy_(buf.tok)
 

@@ -43,6 +43,7 @@ class StepBuffers:
         self.H = z(nbm, B, dims.hidden, dt=act)
         self.conf = z(nbm * B, dt=torch.float32)
         self.arg = z(nbm * B)
+        self.ent = z(nbm * B, dt=torch.float32)
         self.ws = z(max(workspace_bytes(dims), 16), dt=torch.uint8)
         self.bconf = z(nbm, dt=torch.float32)
         self.winner = z(1)

@@ -77,6 +77,16 @@ def test_null_pointers_and_k_rejected():
     assert L.lopa_branch_select(ctypes.byref(d), *([fake] * 9), None, None) == -1
     assert L.lopa_lmhead_conf(None, *([fake] * 8), fake, 1 << 30, None) == -1
     assert L.lopa_synth_qkv(ctypes.byref(d), 1, None, fake, fake, fake, fake, None) == -1
+    # entropy variant: ent is required
+    assert L.lopa_lmhead_conf_ent(ctypes.byref(d), *([fake] * 7), None, None, fake, 1 << 30,
+                                  None) == -1
+    # alpha variant: alpha in [0, 1], every array required
+    for alpha in (-0.1, 1.5, float("nan")):
+        assert L.lopa_branch_select_alpha(ctypes.byref(d), alpha, *([fake] * 13), None) == -1
+    for i in range(13):
+        args = [fake] * 13
+        args[i] = None
+        assert L.lopa_branch_select_alpha(ctypes.byref(d), 0.5, *args, None) == -1
     assert L.lopa_synth_qkv(ctypes.byref(d), 1, fake, fake, fake, None, fake, None) == -1
 
 
@@ -91,8 +101,9 @@ def test_workspace_size_and_shortfall():
     # a long prefix: 16 row groups x 4 heads = 128 workgroups -> 2 splits
     split = _dims(L=4096, B=64, k_max=8)
     assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 64 * 7) * 130 * 4
-    # the LM head alone needs rows x 256 vocabulary parts x (max, sum, argmax)
-    head_need = 5 * 32 * 256 * 12
+    # the LM head alone needs rows x 256 vocabulary parts x (max, sum, argmax,
+    # entropy term)
+    head_need = 5 * 32 * 256 * 16
     fake = ctypes.c_void_p(16)
     L = lopa.lib()
     args = [fake] * 8
@@ -101,4 +112,4 @@ def test_workspace_size_and_shortfall():
     assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
                               need - 1, None) == -3
     f32 = _dims(dtype=lopa.F32, V=1000)
-    assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 12
+    assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 16
