@@ -259,6 +259,104 @@ int lopa_synth_qkv(const lopa_dims* dims, uint64_t seed, const int32_t* br_tok,
 int lopa_commit_block(const lopa_dims* dims, const int32_t* winner, const void* Kb,
                       const void* Vb, void* Kp, void* Vp, int32_t at, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Layer forward of the verification pass (bf16 only).
+ *
+ * The verify stage runs every branch through the model in one pass (news
+ * article, stage 并行验证与复用; "解码效率革命…", section 3.3: one shared matrix
+ * multiply, each branch attending to the original input and its own tokens;
+ * section 6: full-sequence attention).  The model here is a decoder of the
+ * Qwen2.5/Dream-7B family: per layer
+ *   h = RMSNorm(x) g1;  q, k, v = h Wqkv^T + b, q and k rotated;
+ *   x += Attn(q, [prefix K/V of the layer; the branch's own k, v]) Wo^T;
+ *   h = RMSNorm(x) g2;  x += (silu(h Wg^T) * (h Wu^T)) Wd^T
+ * with the embedding of each token (the mask_id row where masked) as x of
+ * the first layer and a final RMSNorm.  Rotary embedding: pairs (i, i+d/2)
+ * of each q/k head turned by (L + p) theta^(-2i/d) for block position p.
+ * RMSNorm: x / sqrt(mean(x^2) + eps) * g.  Attention is lopa_branch_attn's.
+ * Rounding points: the normed rows, q/k/v, the attention output and the
+ * MLP activation are rounded once to bf16 (nearest even); projections
+ * accumulate in float32 into a float32 residual stream.
+ * Rows: all nb_max*B rows (every branch slot) go through the projections;
+ * attention is computed for the live slots b < nb.
+ * ---------------------------------------------------------------------- */
+typedef struct lopa_model_dims {
+  int32_t n_layers;   /* decoder layers, >= 1                                */
+  int32_t inter;      /* MLP intermediate size, multiple of 64               */
+  int32_t mask_id;    /* embedding row of the mask token, 0 <= mask_id < V   */
+  float rope_theta;   /* rotary base, > 1                                    */
+  float rms_eps;      /* RMSNorm epsilon, >= 0                               */
+} lopa_model_dims;
+
+/* Byte offsets in the weight buffer (all tensors bf16, row-major, each
+ * 256-byte aligned).  Layer l's tensor t sits at layer0 + l*layer_stride + t:
+ *   attn_norm [hidden]; wqkv [(Hq+2Hkv)d][hidden] (q rows, then k, then v);
+ *   bqkv [(Hq+2Hkv)d]; wo [hidden][Hq d]; mlp_norm [hidden];
+ *   wgu [2 inter][hidden] (gate rows, then up rows); wd [hidden][inter];
+ * then final_norm [hidden], embed [V][hidden], lm_head [V][hidden]
+ * (lopa_lmhead_conf's W).  total = bytes of the whole buffer. */
+typedef struct lopa_model_layout {
+  size_t attn_norm, wqkv, bqkv, wo, mlp_norm, wgu, wd;
+  size_t layer0, layer_stride;
+  size_t final_norm, embed, lm_head;
+  size_t total;
+} lopa_model_layout;
+
+/* Host only.  LOPA_ERR_INVALID for bad sizes, LOPA_ERR_UNSUPPORTED for f32,
+ * hidden or inter not a multiple of 64, odd d, or a projection too large for
+ * 32-bit offsets. */
+int lopa_model_layout_of(const lopa_dims* dims, const lopa_model_dims* md,
+                         lopa_model_layout* out);
+
+/* Host only: device workspace bytes lopa_branch_forward needs (residual
+ * stream, activations, GEMM partial tiles, attention workspace). */
+int lopa_model_workspace_bytes(const lopa_dims* dims, const lopa_model_dims* md,
+                               size_t* bytes);
+
+/*
+ * Synthetic weights and prefix cache (no trained weights exist here).  Every
+ * element comes from Philox4x32-10 (key = seed low / high 32 bits, counter =
+ * (col/4, row, id | layer << 8, 0); word col%4), with id 0 attn_norm,
+ * 1 wqkv, 2 bqkv, 3 wo, 4 mlp_norm, 5 wgu, 6 wd, 7 final_norm, 8 embed,
+ * 9 lm_head, 10 prefix K, 11 prefix V (rows = prefix positions, columns =
+ * Hkv*d).  Norm weights: 1 + ((x >> 27) - 16) / 128.  Other tensors:
+ * ((x >> 8) - 2^23) * 2^(-24-s) rounded to bf16, with s = round(log2(sqrt(
+ * fan_in / 12))) for the projections and the LM head, 2 for the biases, 1
+ * for the embedding and -1 for the prefix keys and values.
+ * Out weights (lopa_model_layout_of().total bytes); Kp, Vp
+ *     [n_layers][kv_layer_rows][Hkv][d]: rows 0..L-1 of every layer.
+ */
+int lopa_model_synth(const lopa_dims* dims, const lopa_model_dims* md, uint64_t seed,
+                     void* weights, void* Kp, void* Vp, size_t kv_layer_rows,
+                     hipStream_t stream);
+
+/*
+ * One verification forward of every branch's block.
+ * In  weights (layout above); Kp, Vp [n_layers][kv_layer_rows][Hkv][d]
+ *     holding the committed prefix in rows 0..L-1 of each layer;
+ *     br_tok [nb_max*B] (as written by lopa_branch_build), nb[1] (device)
+ * Out Kb, Vb [n_layers][nb_max][B][Hkv][d]: every layer's block keys and
+ *     values of every slot (rotated keys), kept for the commit;
+ *     H [nb_max][B][hidden]: final-normed rows, lopa_lmhead_conf's input.
+ *     ws, ws_bytes: at least lopa_model_workspace_bytes().
+ * Projections stream each weight once for all rows (MFMA, float32
+ * accumulation, split into partial tiles summed by the consumer kernels).
+ */
+int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims* md,
+                        const void* weights, const void* Kp, const void* Vp,
+                        size_t kv_layer_rows, const int32_t* br_tok, const int32_t* nb,
+                        void* Kb, void* Vb, void* H, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * lopa_commit_block for every layer: the winner's slot of Kb, Vb
+ * ([n_layers][nb_max][B][Hkv][d]) copied to rows at .. at+B-1 of each
+ * layer of Kp, Vp ([n_layers][kv_layer_rows][Hkv][d]; at + B <= kv_layer_rows).
+ */
+int lopa_model_commit(const lopa_dims* dims, const lopa_model_dims* md, const int32_t* winner,
+                      const void* Kb, const void* Vb, void* Kp, void* Vp,
+                      size_t kv_layer_rows, int32_t at, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

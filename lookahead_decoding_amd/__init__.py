@@ -47,6 +47,23 @@ class Dims(ctypes.Structure):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class ModelDims(ctypes.Structure):
+    """Mirror of ``lopa_model_dims``."""
+    _fields_ = [("n_layers", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("mask_id", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+    def __repr__(self) -> str:
+        return "ModelDims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class ModelLayout(ctypes.Structure):
+    """Mirror of ``lopa_model_layout`` (byte offsets into the weight buffer)."""
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "attn_norm", "wqkv", "bqkv", "wo", "mlp_norm", "wgu", "wd", "layer0", "layer_stride",
+        "final_norm", "embed", "lm_head", "total")]
+
+
 class LopaError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn} returned {STATUS.get(status, status)}: {text}")
@@ -76,6 +93,17 @@ _SIGS = {
     "lopa_synth_qkv": ([ctypes.POINTER(Dims), ctypes.c_uint64, _P, _P, _P, _P, _P, _P],
                        ctypes.c_int),
     "lopa_commit_block": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _I, _P], ctypes.c_int),
+    "lopa_model_layout_of": ([ctypes.POINTER(Dims), ctypes.POINTER(ModelDims),
+                              ctypes.POINTER(ModelLayout)], ctypes.c_int),
+    "lopa_model_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.POINTER(ModelDims),
+                                    ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "lopa_model_synth": ([ctypes.POINTER(Dims), ctypes.POINTER(ModelDims), ctypes.c_uint64, _P,
+                          _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "lopa_branch_forward": ([ctypes.POINTER(Dims), ctypes.POINTER(ModelDims), _P, _P, _P,
+                             ctypes.c_size_t, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                            ctypes.c_int),
+    "lopa_model_commit": ([ctypes.POINTER(Dims), ctypes.POINTER(ModelDims), _P, _P, _P, _P, _P,
+                           ctypes.c_size_t, _I, _P], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -231,6 +259,50 @@ def lopa_commit_block(dims, winner, Kb, Vb, Kp, Vp, at, stream=None) -> None:
     _check("lopa_commit_block", lib().lopa_commit_block(
         ctypes.byref(dims), _ptr(winner, torch.int32, "winner"), _ptr(Kb, a, "Kb"),
         _ptr(Vb, a, "Vb"), _ptr(Kp, a, "Kp"), _ptr(Vp, a, "Vp"), int(at), _stream(stream)))
+
+
+def model_layout(dims, md) -> ModelLayout:
+    out = ModelLayout()
+    _check("lopa_model_layout_of", lib().lopa_model_layout_of(ctypes.byref(dims), ctypes.byref(md),
+                                                              ctypes.byref(out)))
+    return out
+
+
+def model_workspace_bytes(dims, md) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lopa_model_workspace_bytes", lib().lopa_model_workspace_bytes(
+        ctypes.byref(dims), ctypes.byref(md), ctypes.byref(n)))
+    return n.value
+
+
+def lopa_model_synth(dims, md, seed, weights, Kp, Vp, kv_layer_rows, stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    _check("lopa_model_synth", lib().lopa_model_synth(
+        ctypes.byref(dims), ctypes.byref(md), int(seed) & 0xFFFFFFFFFFFFFFFF,
+        _ptr(weights, torch.uint8, "weights"), _ptr(Kp, bf, "Kp"), _ptr(Vp, bf, "Vp"),
+        int(kv_layer_rows), _stream(stream)))
+
+
+def lopa_branch_forward(dims, md, weights, Kp, Vp, kv_layer_rows, br_tok, nb, Kb, Vb, H, ws,
+                        stream=None) -> None:
+    import torch
+    bf, i32 = torch.bfloat16, torch.int32
+    _check("lopa_branch_forward", lib().lopa_branch_forward(
+        ctypes.byref(dims), ctypes.byref(md), _ptr(weights, torch.uint8, "weights"),
+        _ptr(Kp, bf, "Kp"), _ptr(Vp, bf, "Vp"), int(kv_layer_rows), _ptr(br_tok, i32, "br_tok"),
+        _ptr(nb, i32, "nb"), _ptr(Kb, bf, "Kb"), _ptr(Vb, bf, "Vb"), _ptr(H, bf, "H"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def lopa_model_commit(dims, md, winner, Kb, Vb, Kp, Vp, kv_layer_rows, at, stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    _check("lopa_model_commit", lib().lopa_model_commit(
+        ctypes.byref(dims), ctypes.byref(md), _ptr(winner, torch.int32, "winner"),
+        _ptr(Kb, bf, "Kb"), _ptr(Vb, bf, "Vb"), _ptr(Kp, bf, "Kp"), _ptr(Vp, bf, "Vp"),
+        int(kv_layer_rows), int(at), _stream(stream)))
 
 
 from .step import StepBuffers, run_step, initial_pass  # noqa: E402,F401

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblopa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "build_select.hip", "attn.hip", "lmhead.hip", "synth_qkv.hip"]
+SOURCES = ["api.hip", "build_select.hip", "attn.hip", "lmhead.hip", "synth_qkv.hip", "gemm.hip",
+           "model.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

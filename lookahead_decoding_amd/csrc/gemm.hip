@@ -1,0 +1,184 @@
+// Weight-streaming GEMM of the layer forward: Y[M][N] = X[M][K] W[N][K]^T,
+// bf16 operands, float32 accumulation, for the short activation matrices of
+// a verification pass (M = every branch's block rows, a few hundred at most)
+// against long weights.
+//
+// Section 3.3 of "解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈" has every
+// branch's forward computed in one shared matrix multiply; here all branches'
+// rows ride one stream of each weight, so a weight byte crosses HBM once per
+// pass whatever the number of branches.
+//
+// The work is the iteration space (unit, 64-wide K chunk), cut into equal
+// contiguous ranges, one per workgroup (see GemmView): every compute unit
+// streams the same number of weight bytes however N and K fall, and each
+// workgroup writes float32 partial tiles that the consumer kernels sum.
+// Inside a workgroup the machinery is the LM head's: four producer waves move
+// W and X chunks straight into a three-stage XOR-swizzled LDS ring with
+// buffer loads that write LDS, eight compute waves read
+// v_mfma_f32_32x32x16_bf16 fragments from it.  The activation fragment is the
+// MFMA's A operand, so a lane's outputs run along one weight row and the
+// partial stores are 128-byte row segments.
+#include "gemm_plan.hpp"
+#include "stream_tile.hpp"
+
+namespace lopa {
+
+constexpr int kGemmStage = (256 + 128) * kRB;   // largest BUF of the bodies
+constexpr int kGemmSmem = kStages * kGemmStage;
+
+template <int WX, int NVW, int MTW>
+__device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned short* __restrict__ X,
+                                          const unsigned short* __restrict__ W,
+                                          float* __restrict__ P, unsigned char* smem) {
+  using T = StreamTile<WX, NVW, MTW>;
+  constexpr int WROWS = T::WROWS, HROWS = T::HROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
+  constexpr int KS = kKC / 16;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = blockIdx.x;
+  const int row_bytes = v.K * 2;
+  const long long it0 = v.range_begin(g);
+  const int cnt = static_cast<int>(v.range_begin(g + 1) - it0);
+  if (cnt <= 0) return;
+
+  if (w >= kComputeWaves) {
+    // ---------------- producer waves ----------------
+    const int pw = w - kComputeWaves;
+    const int r8 = lane >> 3;
+    const int ls = (lane & 7) ^ r8 ^ (pw & 1);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(W), 0, v.N * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(X), 0, v.M * row_bytes, 0x00020000);
+    const int wv = (8 * pw + r8) * row_bytes + ls * 16;
+    auto issue = [&](int j) __attribute__((always_inline)) {
+      unsigned char* dst = smem + (j % kStages) * BUF;
+      j = min(j, cnt - 1);
+      const long long it = it0 + j;
+      const int u = static_cast<int>(it / v.nch);
+      const int kc = static_cast<int>(it - static_cast<long long>(u) * v.nch);
+      const int wb = u / v.groups;
+      const int grp = u - wb * v.groups;
+      const int sw = wb * WROWS * row_bytes + kc * kRB;
+#pragma unroll
+      for (int p = 0; p < WP; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + pw) * 1024), 16, wv,
+                                                 sw + 32 * p * row_bytes, 0, kWeightAux);
+#pragma unroll
+      for (int p = 0; p < HP; ++p) {
+        const int row = min(grp * HROWS + 8 * (4 * p + pw) + r8, v.M - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, LOPA_LDS(dst + WROWS * kRB + (4 * p + pw) * 1024), 16,
+            row * row_bytes + ls * 16, kc * kRB, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u) issue(u);
+    wait_vmcnt<(kStages - 2) * (WP + HP)>();
+    __builtin_amdgcn_s_barrier();
+    for (int i = 0; i + 1 < cnt; ++i) {
+      issue(i + kStages - 1);
+      wait_vmcnt<(kStages - 2) * (WP + HP)>();
+      __builtin_amdgcn_s_barrier();
+    }
+    wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+  } else {
+    // ---------------- compute waves ----------------
+    const int wx = w % WX;
+    const int wy = w / WX;
+    const int ln = lane & 31;
+    const int lh = lane >> 5;
+    f32x16 acc[MTW][NVW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
+    auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NVW], u16x8 (&hf)[MTW])
+        __attribute__((always_inline)) {
+      const int s = j * 2 + lh;
+#pragma unroll
+      for (int n = 0; n < NVW; ++n) {
+        const int r = (wx * NVW + n) * 32 + ln;
+        wf[n] = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        const int r = (wy * MTW + mt) * 32 + ln;
+        hf[mt] = *reinterpret_cast<const u16x8*>(base + (WROWS + r) * kRB + swz<kKC>(r, s) * 16);
+      }
+    };
+    auto compute = [&](int b) __attribute__((always_inline)) {
+      const unsigned char* base = smem + b * BUF;
+      u16x8 wf[2][NVW], hf[2][MTW];
+      frags(base, 0, wf[0], hf[0]);
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        if (j + 1 < KS) frags(base, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+          for (int n = 0; n < NVW; ++n)
+            acc[mt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, hf[j & 1][mt]), __builtin_bit_cast(bf16x8, wf[j & 1][n]),
+                acc[mt][n], 0, 0, 0);
+      }
+    };
+    // acc[mt][n][q] = Y[row (wy*MTW + mt)*32 + 8(q/4) + 4lh + q%4 of the group]
+    //                  [col (wx*NVW + n)*32 + ln of the weight block]
+    auto flush = [&](int u) {
+      const int wb = u / v.groups;
+      const int grp = u - wb * v.groups;
+      const int slot = g - v.first_wg(u);
+      const int mg = min(v.M - grp * HROWS, HROWS);
+      const int ng = min(v.N - wb * WROWS, WROWS);
+      float* tile = P + v.at(u, slot, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int n = 0; n < NVW; ++n) {
+          const int c = (wx * NVW + n) * 32 + ln;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = (wy * MTW + mt) * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
+            if (r < mg && c < ng) tile[r * WROWS + c] = acc[mt][n][q];
+          }
+          acc[mt][n] = f32x16{};
+        }
+    };
+    for (int i = 0; i < cnt; ++i) {
+      __syncthreads();
+      const long long it = it0 + i;
+      const int u = static_cast<int>(it / v.nch);
+      const int kc = static_cast<int>(it - static_cast<long long>(u) * v.nch);
+      const int grp = u % v.groups;
+      // a wave whose activation tiles all lie past the last row only keeps step
+      if (grp * HROWS + wy * MTW * 32 < v.M) {
+        compute(i % kStages);
+        if (kc == v.nch - 1 || i == cnt - 1) flush(u);
+      }
+    }
+  }
+}
+
+template <int WX, int NVW, int MTW>
+__global__ void __launch_bounds__(kStreamThreads)
+k_gemm_stream(GemmView v, const unsigned short* __restrict__ X,
+              const unsigned short* __restrict__ W, float* __restrict__ P) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kGemmSmem];
+  gemm_body<WX, NVW, MTW>(v, X, W, P, smem);
+}
+
+// Enqueue Y = X W^T as partial tiles into P (v.partial_bytes() bytes).
+int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short* W, float* P,
+                hipStream_t stream) {
+  const dim3 grid(v.G), block(kStreamThreads);
+  switch (v.body) {
+    case 0: hipLaunchKernelGGL((k_gemm_stream<4, 2, 1>), grid, block, 0, stream, v, X, W, P); break;
+    case 1: hipLaunchKernelGGL((k_gemm_stream<4, 2, 2>), grid, block, 0, stream, v, X, W, P); break;
+    default: hipLaunchKernelGGL((k_gemm_stream<2, 2, 2>), grid, block, 0, stream, v, X, W, P); break;
+  }
+  return hipGetLastError() == hipSuccess ? LOPA_OK : LOPA_ERR_HIP;
+}
+
+}  // namespace lopa

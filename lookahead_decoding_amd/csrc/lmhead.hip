@@ -27,6 +27,7 @@
 //                   per vocabulary entry, FMA dot products.
 #include "lopa_common.hpp"
 #include "head_plan.hpp"
+#include "stream_tile.hpp"
 
 namespace lopa {
 
@@ -34,15 +35,6 @@ namespace lopa {
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
-
-// Physical 16-byte slot of logical slot s in LDS row r.  Rows of a K chunk
-// are KC*2 bytes; the XOR keeps 16-lane fragment reads (16 consecutive rows,
-// one slot) and the staging writes free of bank conflicts.
-template <int KC>
-__device__ __forceinline__ int swz(int r, int s) {
-  if constexpr (KC == 64) return s ^ ((r & 7) ^ ((r >> 3) & 1));
-  else return s ^ (((r >> 1) ^ (r >> 2)) & 3);
-}
 
 // Online-softmax partial of one lane's logits for one LM-head row:
 // a[n][r] = logit of vocabulary entry vb + 32n + 8(r/4) + 4h + r%4 (the
@@ -81,43 +73,10 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
   return merge(p, shfl_xor(p, 32));
 }
 
-constexpr int kKC = 64;          // K chunk
-constexpr int kRB = kKC * 2;     // bytes of one row per chunk (8 slots of 16 B)
-constexpr int kStages = 3;       // LDS stages: S - 1 chunks in flight while one is computed
 constexpr int kRunRows = 512;    // running partials: compute-wave columns x rows
-// Cache policy of the weight loads: non-temporal.  Measured faster than
-// normal caching in every layout, also where row groups share the weight
-// through L2 (prefix 512: 212 vs 232 us per call).
-constexpr int kWeightAux = 2;
-constexpr int kComputeWaves = 8; // two per SIMD, so one wave's LDS reads hide under the other's MFMAs
-constexpr int kLoadWaves = 4;
-constexpr int kHeadThreads = 64 * (kComputeWaves + kLoadWaves);
-
-// Shape of one body: WX x (kComputeWaves / WX) compute waves over
-// (vocabulary, rows); each wave holds NVW 32-row vocabulary tiles against MTW
-// 32-row tiles of H.
-template <int WX, int NVW, int MTW>
-struct HeadTile {
-  static constexpr int WY = kComputeWaves / WX;
-  static constexpr int WROWS = WX * NVW * 32;       // vocabulary rows per pass
-  static constexpr int HROWS = WY * MTW * 32;       // LM-head rows staged per chunk
-  static constexpr int BUF = (WROWS + HROWS) * kRB; // bytes per LDS stage
-  static constexpr int WP = WROWS / 32;             // W DMA loads per producer wave per chunk
-  static constexpr int HP = HROWS / 32;             // H DMA loads per producer wave per chunk
-  static constexpr int RUNS = kRunRows / WX;        // running-partial stride per wave column
-  static_assert(HROWS <= RUNS, "running partials");
-};
+constexpr int kHeadThreads = kStreamThreads;
 constexpr int kHeadStage = (256 + 128) * kRB;        // largest BUF of the bodies below
 constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(sizeof(Partial));
-
-// s_waitcnt on the vector-memory counter only (lgkm and exp counts left open).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-#define LOPA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // One persistent workgroup owns a contiguous, balanced vocabulary range
 // (multiples of 16 rows) of its part and the Mg rows of its row group; it
@@ -149,8 +108,10 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
                                           float* __restrict__ ws_m, float* __restrict__ ws_s,
                                           int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
                                           float* __restrict__ logits_out) {
-  using T = HeadTile<WX, NVW, MTW>;
+  using T = StreamTile<WX, NVW, MTW>;
   constexpr int WROWS = T::WROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
+  constexpr int RUNS = kRunRows / WX;   // running-partial stride per wave column
+  static_assert(T::HROWS <= RUNS, "running partials");
   constexpr int KS = kKC / 16;   // MFMA K steps per chunk
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -265,9 +226,9 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
         const Partial p = row_partial<NVW, ENT>(acc[mt], vbw, lh, v_hi);
         const int r = (wy * MTW + mt) * 32 + ln;
         if (lh == 0) {
-          Partial q = merge(run[wx * T::RUNS + r], p);
+          Partial q = merge(run[wx * RUNS + r], p);
           if constexpr (!ENT) q.t = 0.f;   // keeps the entropy arithmetic out
-          run[wx * T::RUNS + r] = q;
+          run[wx * RUNS + r] = q;
         }
         if (logits_out && r < Mg) {
           const size_t lb = static_cast<size_t>(rows[row0 + r]) * V;
@@ -293,7 +254,7 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   for (int r = tid; r < Mg; r += kHeadThreads) {
     Partial p = run[r];
 #pragma unroll
-    for (int x = 1; x < WX; ++x) p = merge(p, run[x * T::RUNS + r]);
+    for (int x = 1; x < WX; ++x) p = merge(p, run[x * RUNS + r]);
     const size_t o = static_cast<size_t>(row0 + r) * nparts + part;
     ws_m[o] = p.m;
     ws_s[o] = p.s;

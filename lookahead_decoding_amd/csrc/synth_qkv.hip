@@ -21,31 +21,9 @@
 // Counters of element (slot b, position p, head h, dimension e) of tensor
 // kind (0 Q, 1 K, 2 V): (p | kind << 8 | h << 16, token as uint32, e, draw);
 // key (seed low 32 bits, seed high 32 bits).
-#include "lopa_common.hpp"
+#include "philox.hpp"
 
 namespace lopa {
-
-struct U32x4 {
-  unsigned x0, x1, x2, x3;
-};
-
-__device__ __forceinline__ U32x4 philox4x32_10(U32x4 c, unsigned k0, unsigned k1) {
-  constexpr unsigned M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
-  constexpr unsigned W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += W0;
-      k1 += W1;
-    }
-    const unsigned long long p0 = static_cast<unsigned long long>(M0) * c.x0;
-    const unsigned long long p1 = static_cast<unsigned long long>(M1) * c.x2;
-    const unsigned hi0 = static_cast<unsigned>(p0 >> 32), lo0 = static_cast<unsigned>(p0);
-    const unsigned hi1 = static_cast<unsigned>(p1 >> 32), lo1 = static_cast<unsigned>(p1);
-    c = U32x4{hi1 ^ c.x1 ^ k0, lo1, hi0 ^ c.x3 ^ k1, lo0};
-  }
-  return c;
-}
 
 __device__ __forceinline__ unsigned halves_sum(unsigned w) { return (w & 0xFFFFu) + (w >> 16); }
 
