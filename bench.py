@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the oracle's timed CPU work")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the step with the 28-layer model forward")
+    ap.add_argument("--model-steps", type=int, default=30)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run 3 device copies of 1 GiB (a reference for byte counters)")
     return ap.parse_args()
@@ -112,6 +115,104 @@ def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10, alpha=N
     ms = (time.perf_counter() - t0) / reps * 1e3
     return {"k": k, "alpha": alpha, "masked": m, "steps": steps, "tpf": round(m / steps, 3),
             "ms_per_block": round(ms, 3), "decoded_tokens_per_s": round(m / (ms * 1e-3), 1)}
+
+
+def model_bytes(dims, md) -> dict:
+    """Algorithmic bytes of one lopa_branch_forward: every weight once, the
+    embedding rows, each layer's prefix K/V, the block K/V and H written."""
+    hid, e = dims.hidden, 2
+    qkv = (dims.Hq + 2 * dims.Hkv) * dims.d
+    M = dims.nb_max * dims.B
+    layer_w = (qkv * hid + qkv + hid * hid + 2 * hid + 2 * md.inter * hid + hid * md.inter) * e
+    kv = 2 * dims.Hkv * dims.d * e
+    fwd = md.n_layers * (layer_w + dims.L * kv + M * kv) + hid * e + 2 * M * hid * e
+    return dict(forward_bytes=fwd, weight_bytes=md.n_layers * layer_w + hid * e,
+                flops=2.0 * M * (md.n_layers * layer_w / e))
+
+
+def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
+    """A verification step with the 28-layer Qwen2.5/Dream-7B-shaped forward
+    (synthetic weights): build -> lopa_branch_forward -> lopa_lmhead_conf
+    (the model's LM head) -> select; and the same with one branch (k_max 0)
+    for the cost of the extra branches."""
+    import torch
+    import lookahead_decoding_amd as lopa
+    from lookahead_decoding_amd.model import QWEN7B, ForwardBuffers, Model, forward, model_dims
+    from lookahead_decoding_amd.step import StepBuffers, dims_of, to_device
+
+    md = model_dims(**QWEN7B)
+    out = {"model": "Qwen2.5/Dream-7B geometry, 28 layers, synthetic bf16 weights (Philox)",
+           "weights_gb": None}
+
+    def run(k_max: int, k: int) -> dict:
+        dims = dims_of(cfg)
+        dims.k_max = k_max
+        model = Model(dims, md, seed=0x7B00 + inp.seed)
+        out["weights_gb"] = round(model.layout.total / 1e9, 2)
+        buf, fb = StepBuffers(dims), ForwardBuffers(dims, md)
+        stream = torch.cuda.current_stream()
+        B, nbm = dims.B, dims.nb_max
+        # the state a step starts from: slot 0 alone through the model, LM head on the masked rows
+        tok = np.asarray(inp.tok, np.int32)
+        masked = np.flatnonzero(tok == lopa.MASK).astype(np.int32)
+        rows = np.zeros(nbm * B, np.int32)
+        rows[:len(masked)] = masked
+        row_ptr = np.full(nbm + 1, len(masked), np.int32)
+        row_ptr[0] = 0
+        one = to_device(np.array([1], np.int32))
+        forward(model, to_device(np.tile(tok, nbm)), one, fb, dims=dims)
+        lopa.lopa_lmhead_conf(dims, fb.H, model.lm_head, to_device(rows), to_device(row_ptr), one,
+                              buf.conf, buf.arg, None, buf.ws)
+        conf = buf.conf[:B].clone()
+        arg = buf.arg[:B].clone()
+        tk = to_device(tok)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+        def step(e=None):
+            lopa.lopa_branch_build(dims, k, cfg.tau, tk, conf, arg, buf.nb, buf.br_tok,
+                                   buf.br_mask, buf.rows, buf.row_ptr)
+            if e is not None:
+                e[0].record(stream)
+            forward(model, buf.br_tok, buf.nb, fb, dims=dims)
+            if e is not None:
+                e[1].record(stream)
+            lopa.lopa_lmhead_conf(dims, fb.H, model.lm_head, buf.rows, buf.row_ptr, buf.nb,
+                                  buf.conf, buf.arg, None, buf.ws)
+            if e is not None:
+                e[2].record(stream)
+            lopa.lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg,
+                                    buf.bconf, buf.winner, buf.tok_next, buf.conf_next,
+                                    buf.arg_next)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        head_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        alg = model_bytes(dims, md)
+        ach = alg["forward_bytes"] / (fwd_ms * 1e-3) / 1e9
+        res = {"k": k, "branches": int(buf.nb.item()), "rows": nbm * B,
+               "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 3),
+               "forward_ms": round(fwd_ms, 3), "lmhead_ms": round(head_ms, 3),
+               "forward_roofline": {"bound": "hbm", "achieved": round(ach, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                                    "algorithmic_bytes": alg["forward_bytes"],
+                                    "mfma_tflops": round(alg["flops"] / (fwd_ms * 1e-3) / 1e12, 1)}}
+        del model, buf, fb
+        torch.cuda.empty_cache()
+        return res
+
+    out["lookahead"] = run(cfg.k, cfg.k)
+    out["one_branch"] = run(0, 0)
+    out["extra_branch_cost"] = round(out["lookahead"]["ms_per_step"] /
+                                     out["one_branch"]["ms_per_step"] - 1.0, 4)
+    return out
 
 
 def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
@@ -306,6 +407,8 @@ def main():
             "anchor_only": decode_measure(dims, cfg, inp, x, 0, seed),
             "lookahead_alpha_0.5": decode_measure(dims, cfg, inp, x, cfg.k, seed, alpha=0.5),
         }
+    if not args.no_model and cfg.dtype == "bf16":
+        out["model_step"] = model_measure(cfg, inp, args.model_steps, 5)
     if not args.no_cpu_baseline:
         import oracle as O  # noqa: F401  (CPU baseline leg only)
         c, a, _ = O.initial_state(inp)

@@ -303,7 +303,7 @@ typedef struct lopa_model_layout {
 } lopa_model_layout;
 
 /* Host only.  LOPA_ERR_INVALID for bad sizes, LOPA_ERR_UNSUPPORTED for f32,
- * hidden or inter not a multiple of 64, odd d, or a projection too large for
+ * hidden or inter not a multiple of 64, d not a multiple of 8, or a projection too large for
  * 32-bit offsets. */
 int lopa_model_layout_of(const lopa_dims* dims, const lopa_model_dims* md,
                          lopa_model_layout* out);

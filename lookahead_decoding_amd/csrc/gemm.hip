@@ -38,8 +38,8 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
   const int lane = tid & 63;
   const int g = blockIdx.x;
   const int row_bytes = v.K * 2;
-  const long long it0 = v.range_begin(g);
-  const int cnt = static_cast<int>(v.range_begin(g + 1) - it0);
+  const int it0 = v.range_begin(g);
+  const int cnt = v.range_begin(g + 1) - it0;
   if (cnt <= 0) return;
 
   if (w >= kComputeWaves) {
@@ -55,9 +55,9 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
     auto issue = [&](int j) __attribute__((always_inline)) {
       unsigned char* dst = smem + (j % kStages) * BUF;
       j = min(j, cnt - 1);
-      const long long it = it0 + j;
-      const int u = static_cast<int>(it / v.nch);
-      const int kc = static_cast<int>(it - static_cast<long long>(u) * v.nch);
+      const int it = it0 + j;
+      const int u = it / v.nch;
+      const int kc = it - u * v.nch;
       const int wb = u / v.groups;
       const int grp = u - wb * v.groups;
       const int sw = wb * WROWS * row_bytes + kc * kRB;
@@ -148,9 +148,9 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
     };
     for (int i = 0; i < cnt; ++i) {
       __syncthreads();
-      const long long it = it0 + i;
-      const int u = static_cast<int>(it / v.nch);
-      const int kc = static_cast<int>(it - static_cast<long long>(u) * v.nch);
+      const int it = it0 + i;
+      const int u = it / v.nch;
+      const int kc = it - u * v.nch;
       const int grp = u % v.groups;
       // a wave whose activation tiles all lie past the last row only keeps step
       if (grp * HROWS + wy * MTW * 32 < v.M) {

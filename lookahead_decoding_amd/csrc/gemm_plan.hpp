@@ -3,55 +3,81 @@
 // same view is handed to the kernels that consume the partial sums.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace lopa {
 
 constexpr int kGemmMaxWorkgroups = 256;   // one per compute unit
+constexpr int kSlotTableMax = 4096;       // units whose slot counts a consumer keeps in LDS
 
 // The iteration space is (unit, K chunk) with unit = (weight block of WROWS
 // rows, activation row group of HROWS rows), weight-block major.  It is cut
-// into G equal contiguous ranges, one per workgroup ("stream-K"): a
-// workgroup walks its range, and whenever its unit changes (or its range
-// ends) it writes the unit's partial sum as one float32 tile into slot
-// g - first_wg(unit) of that unit.  Summing a unit's slots gives its tile of
-// Y; every slot of every unit is written exactly once.
+// into G contiguous ranges, one per workgroup ("stream-K"): the first r = I
+// mod G ranges hold q + 1 iterations, the rest q = I / G.  A workgroup walks
+// its range, and whenever its unit changes (or its range ends) it writes the
+// unit's partial sum as one float32 tile into slot g - first_wg(unit) of
+// that unit.  Summing a unit's slots gives its tile of Y; every slot of every
+// unit is written exactly once.
 struct GemmView {
   int M, N, K;
-  int body;       // 0: 64 activation rows x 256 weight rows per pass; 1: 128 x 256; 2: 256 x 128
+  // activation rows x weight rows per pass: 0: 64 x 256; 1: 128 x 256; 2: 256 x 128
+  int body;
   int hrows, wrows;
+  int hshift, wshift;   // log2 of hrows, wrows
   int groups;     // activation row groups
   int units;      // weight blocks x groups
   int nch;        // K / 64
   int G;          // workgroups
   int smax;       // most slots any unit has
-  long long iters;
+  int iters;      // units * nch
+  int q, r;       // iterations per range: q + 1 for the first r ranges, then q
 
-  // first / last workgroup whose range holds iteration x: the largest g
-  // with floor(g * iters / G) <= x
-  __host__ __device__ int owner(long long x) const {
-    return static_cast<int>(((x + 1) * G + iters - 1) / iters) - 1;
+  __host__ __device__ int range_begin(int g) const { return g * q + (g < r ? g : r); }
+  // the workgroup whose range holds iteration x
+  __host__ __device__ int owner(int x) const {
+    const int big = r * (q + 1);
+    return x < big ? x / (q + 1) : r + (x - big) / q;
   }
-  __host__ __device__ int first_wg(int u) const { return owner(static_cast<long long>(u) * nch); }
-  __host__ __device__ int last_wg(int u) const {
-    return owner(static_cast<long long>(u + 1) * nch - 1);
-  }
-  __host__ __device__ long long range_begin(int g) const { return g * iters / G; }
+  __host__ __device__ int first_wg(int u) const { return owner(u * nch); }
+  __host__ __device__ int last_wg(int u) const { return owner((u + 1) * nch - 1); }
   __host__ __device__ size_t tile_elems() const { return static_cast<size_t>(hrows) * wrows; }
   // element (row, col) of slot s of unit u
   __host__ __device__ size_t at(int u, int s, int row_local, int col_local) const {
     return (static_cast<size_t>(u) * smax + s) * tile_elems() +
            static_cast<size_t>(row_local) * wrows + col_local;
   }
-  // Y[row][col] = sum over the slots of its unit
-  __host__ __device__ float sum(const float* P, int row, int col) const {
-    const int grp = row / hrows, wb = col / wrows;
+  // Consumers first write every unit's slot count into an LDS table (units
+  // <= kSlotTableMax), then sum a unit's slots in slot order.
+  __device__ void load_slots(unsigned char* tab) const {
+    for (int u = threadIdx.x; u < units; u += blockDim.x)
+      tab[u] = static_cast<unsigned char>(last_wg(u) - first_wg(u) + 1);
+  }
+  // Y[row][col .. col+3] (col % 4 == 0; the four columns share a unit); the
+  // slot loads are issued four at a time before any is added.
+  __device__ float4 sum4(const float* __restrict__ P, const unsigned char* tab, int row,
+                         int col) const {
+    const int grp = row >> hshift, wb = col >> wshift;
     const int u = wb * groups + grp;
-    const int s1 = last_wg(u) - first_wg(u);
-    const int rl = row - grp * hrows, cl = col - wb * wrows;
-    float y = 0.f;
-    for (int s = 0; s <= s1; ++s) y += P[at(u, s, rl, cl)];
+    const int ns = tab[u];
+    const float4* p = reinterpret_cast<const float4*>(
+        P + at(u, 0, row - (grp << hshift), col - (wb << wshift)));
+    const size_t stride = tile_elems() / 4;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+      float4 t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        t[j] = s0 + j < ns ? p[(s0 + j) * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y.x += t[j].x;
+        y.y += t[j].y;
+        y.z += t[j].z;
+        y.w += t[j].w;
+      }
+    }
     return y;
   }
   size_t partial_bytes() const { return static_cast<size_t>(units) * smax * tile_elems() * 4; }
@@ -69,12 +95,17 @@ inline GemmView gemm_view(int M, int N, int K, int max_wgs = kGemmMaxWorkgroups)
   } else {
     v.body = 2; v.hrows = 256; v.wrows = 128;
   }
+  v.hshift = v.hrows == 64 ? 6 : (v.hrows == 128 ? 7 : 8);
+  v.wshift = v.wrows == 128 ? 7 : 8;
   v.groups = (M + v.hrows - 1) / v.hrows;
   v.units = ((N + v.wrows - 1) / v.wrows) * v.groups;
   v.nch = K / 64;
-  v.iters = static_cast<long long>(v.units) * v.nch;
-  v.G = static_cast<int>(v.iters < max_wgs ? v.iters : max_wgs);
+  const long long iters = static_cast<long long>(v.units) * v.nch;
+  v.iters = static_cast<int>(iters);   // callers keep units * nch below 2^31
+  v.G = static_cast<int>(iters < max_wgs ? iters : max_wgs);
   if (v.G < 1) v.G = 1;
+  v.q = v.iters / v.G;
+  v.r = v.iters - v.q * v.G;
   v.smax = 1;
   for (int u = 0; u < v.units; ++u) {
     const int s = v.last_wg(u) - v.first_wg(u) + 1;

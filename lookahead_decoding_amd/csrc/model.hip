@@ -77,14 +77,23 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 }
 
 // h[r] = bf16(x[r] / sqrt(mean(x[r]^2) + eps) * g) for the float32 row x[r]
-// this thread has just written (the same thread re-reads its own elements).
+// this thread has just written (the same thread re-reads its own elements,
+// four at a time: hidden is a multiple of 64).
 __device__ __forceinline__ void norm_row(const float* __restrict__ xr, float ss, int hidden,
                                          float eps, const unsigned short* __restrict__ g,
                                          unsigned short* __restrict__ hr, float* red) {
   const float tot = block_sum_256(ss, red);
   const float rs = 1.f / sqrtf(tot / static_cast<float>(hidden) + eps);
-  for (int n = threadIdx.x; n < hidden; n += 256)
-    hr[n] = f32_to_bf16_bits(xr[n] * rs * bf16_bits_to_f32(g[n]));
+  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+    const float4 x = *reinterpret_cast<const float4*>(xr + n);
+    const ushort4 gg = *reinterpret_cast<const ushort4*>(g + n);
+    ushort4 o;
+    o.x = f32_to_bf16_bits(x.x * rs * bf16_bits_to_f32(gg.x));
+    o.y = f32_to_bf16_bits(x.y * rs * bf16_bits_to_f32(gg.y));
+    o.z = f32_to_bf16_bits(x.z * rs * bf16_bits_to_f32(gg.z));
+    o.w = f32_to_bf16_bits(x.w * rs * bf16_bits_to_f32(gg.w));
+    *reinterpret_cast<ushort4*>(hr + n) = o;
+  }
 }
 
 // Embedding of each row's token (the mask token's row where masked) into the
@@ -100,10 +109,15 @@ k_embed_norm(int hidden, int V, int mask_id, float eps, const int32_t* __restric
   float* xr = x + static_cast<size_t>(r) * hidden;
   const unsigned short* er = E + static_cast<size_t>(e) * hidden;
   float ss = 0.f;
-  for (int n = threadIdx.x; n < hidden; n += 256) {
-    const float v = bf16_bits_to_f32(er[n]);
-    xr[n] = v;
-    ss = fmaf(v, v, ss);
+  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+    const ushort4 ev = *reinterpret_cast<const ushort4*>(er + n);
+    const float4 v = make_float4(bf16_bits_to_f32(ev.x), bf16_bits_to_f32(ev.y),
+                                 bf16_bits_to_f32(ev.z), bf16_bits_to_f32(ev.w));
+    *reinterpret_cast<float4*>(xr + n) = v;
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
   }
   norm_row(xr, ss, hidden, eps, g, h + static_cast<size_t>(r) * hidden, red);
 }
@@ -115,45 +129,79 @@ k_residual_norm(GemmView v, const float* __restrict__ P, float eps,
                 const unsigned short* __restrict__ g, float* __restrict__ x,
                 unsigned short* __restrict__ h) {
   __shared__ float red[4];
+  __shared__ unsigned char tab[kSlotTableMax];
+  v.load_slots(tab);
+  __syncthreads();
   const int r = blockIdx.x;
   const int hidden = v.N;
   float* xr = x + static_cast<size_t>(r) * hidden;
   float ss = 0.f;
-  for (int n = threadIdx.x; n < hidden; n += 256) {
-    const float y = xr[n] + v.sum(P, r, n);
-    xr[n] = y;
-    ss = fmaf(y, y, ss);
+  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+    float4 y = *reinterpret_cast<const float4*>(xr + n);
+    const float4 d = v.sum4(P, tab, r, n);
+    y.x += d.x;
+    y.y += d.y;
+    y.z += d.z;
+    y.w += d.w;
+    *reinterpret_cast<float4*>(xr + n) = y;
+    ss = fmaf(y.x, y.x, ss);
+    ss = fmaf(y.y, y.y, ss);
+    ss = fmaf(y.z, y.z, ss);
+    ss = fmaf(y.w, y.w, ss);
   }
   norm_row(xr, ss, hidden, eps, g, h + static_cast<size_t>(r) * hidden, red);
 }
 
-// q/k/v of row r: projection + bias; q and k rotated by the position's angles
-// (pairs (i, i + d/2), angle (L + r % B) * theta^(-2i/d), evaluated in double
-// and rounded to float once); all three rounded to bf16.  One thread per
-// (row, head, i < d/2); heads 0..Hq-1 are q's, then k's, then v's.
+// Rotary table of the block's positions: (cos, sin) of (L + p) * theta^(-2i/d)
+// for p < B, i < d/2, evaluated in double and rounded to float once.
 __global__ void __launch_bounds__(256)
-k_qkv_epilogue(GemmView v, const float* __restrict__ P, int B, int L, int Hq, int Hkv, int d,
-               double log2_theta, const unsigned short* __restrict__ bias,
+k_rope_table(int B, int L, int d, double log2_theta, float2* __restrict__ tab) {
+  const int half = d >> 1;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * half) return;
+  const int p = idx / half, i = idx - p * half;
+  const double ang =
+      static_cast<double>(L + p) * exp2(-2.0 * static_cast<double>(i) / d * log2_theta);
+  tab[idx] = make_float2(static_cast<float>(cos(ang)), static_cast<float>(sin(ang)));
+}
+
+// q/k/v of row r: projection + bias; q and k turned by the rotary table
+// (pairs (i, i + d/2)); all three rounded to bf16.  One thread per (row,
+// head, 4 consecutive i < d/2); heads 0..Hq-1 are q's, then k's, then v's.
+// d is a multiple of 8.
+__global__ void __launch_bounds__(256)
+k_qkv_epilogue(GemmView v, const float* __restrict__ P, int B, int Hq, int Hkv, int d,
+               const float2* __restrict__ rope, const unsigned short* __restrict__ bias,
                unsigned short* __restrict__ Q, unsigned short* __restrict__ K,
                unsigned short* __restrict__ Vo) {
-  const int half = d >> 1;
+  __shared__ unsigned char tab[kSlotTableMax];
+  v.load_slots(tab);
+  __syncthreads();
+  const int half = d >> 1, quads = half >> 2;
   const int heads = Hq + 2 * Hkv;
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long long>(v.M) * heads * half) return;
-  const int i = static_cast<int>(idx % half);
-  const int hh = static_cast<int>((idx / half) % heads);
-  const int r = static_cast<int>(idx / (static_cast<long long>(half) * heads));
-  const int ni = hh * d + i, nj = ni + half;
-  float a = v.sum(P, r, ni) + bf16_bits_to_f32(bias[ni]);
-  float b = v.sum(P, r, nj) + bf16_bits_to_f32(bias[nj]);
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= v.M * heads * quads) return;
+  const int i0 = 4 * (idx % quads);
+  const int hh = (idx / quads) % heads;
+  const int r = idx / (quads * heads);
+  const int ni = hh * d + i0, nj = ni + half;
+  const float4 pa = v.sum4(P, tab, r, ni), pb = v.sum4(P, tab, r, nj);
+  float a[4] = {pa.x, pa.y, pa.z, pa.w}, b[4] = {pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] += bf16_bits_to_f32(bias[ni + j]);
+    b[j] += bf16_bits_to_f32(bias[nj + j]);
+  }
   if (hh < Hq + Hkv) {
-    const double ang =
-        static_cast<double>(L + r % B) * exp2(-2.0 * static_cast<double>(i) / d * log2_theta);
-    const float c = static_cast<float>(cos(ang)), s = static_cast<float>(sin(ang));
-    const float a2 = a * c - b * s;
-    const float b2 = b * c + a * s;
-    a = a2;
-    b = b2;
+    const float2* cs = rope + (r % B) * half + i0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float c = cs[j].x, s = cs[j].y;
+      const float a2 = a[j] * c - b[j] * s;
+      const float b2 = b[j] * c + a[j] * s;
+      a[j] = a2;
+      b[j] = b2;
+    }
   }
   unsigned short* dst;
   size_t base;
@@ -167,21 +215,35 @@ k_qkv_epilogue(GemmView v, const float* __restrict__ P, int B, int L, int Hq, in
     dst = Vo;
     base = (static_cast<size_t>(r) * Hkv + (hh - Hq - Hkv)) * d;
   }
-  dst[base + i] = f32_to_bf16_bits(a);
-  dst[base + i + half] = f32_to_bf16_bits(b);
+  ushort4 oa, ob;
+  oa.x = f32_to_bf16_bits(a[0]); oa.y = f32_to_bf16_bits(a[1]);
+  oa.z = f32_to_bf16_bits(a[2]); oa.w = f32_to_bf16_bits(a[3]);
+  ob.x = f32_to_bf16_bits(b[0]); ob.y = f32_to_bf16_bits(b[1]);
+  ob.z = f32_to_bf16_bits(b[2]); ob.w = f32_to_bf16_bits(b[3]);
+  *reinterpret_cast<ushort4*>(dst + base + i0) = oa;
+  *reinterpret_cast<ushort4*>(dst + base + i0 + half) = ob;
 }
 
-// act[r][j] = bf16(silu(gate) * up), gate = column j and up = column
-// inter + j of the gate/up projection.
+// act[r][j..j+3] = bf16(silu(gate) * up), gate = columns j.. and up = columns
+// inter + j.. of the gate/up projection (inter is a multiple of 64).
 __global__ void __launch_bounds__(256)
 k_swiglu(GemmView v, const float* __restrict__ P, int inter, unsigned short* __restrict__ act) {
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long long>(v.M) * inter) return;
-  const int r = static_cast<int>(idx / inter);
-  const int j = static_cast<int>(idx - static_cast<long long>(r) * inter);
-  const float gt = v.sum(P, r, j);
-  const float up = v.sum(P, r, inter + j);
-  act[idx] = f32_to_bf16_bits(gt / (1.f + expf(-gt)) * up);
+  __shared__ unsigned char tab[kSlotTableMax];
+  v.load_slots(tab);
+  __syncthreads();
+  const int q4 = inter >> 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= v.M * q4) return;
+  const int r = idx / q4;
+  const int j = 4 * (idx - r * q4);
+  const float4 gt = v.sum4(P, tab, r, j);
+  const float4 up = v.sum4(P, tab, r, inter + j);
+  ushort4 o;
+  o.x = f32_to_bf16_bits(gt.x / (1.f + expf(-gt.x)) * up.x);
+  o.y = f32_to_bf16_bits(gt.y / (1.f + expf(-gt.y)) * up.y);
+  o.z = f32_to_bf16_bits(gt.z / (1.f + expf(-gt.z)) * up.z);
+  o.w = f32_to_bf16_bits(gt.w / (1.f + expf(-gt.w)) * up.w);
+  *reinterpret_cast<ushort4*>(act + static_cast<size_t>(r) * inter + j) = o;
 }
 
 // Copy of the winner's block K/V slot of every layer to the prefix rows
@@ -217,11 +279,16 @@ static int check_model(const lopa_dims* d, const lopa_model_dims* md) {
   if (!(md->rope_theta > 1.f) || !(md->rms_eps >= 0.f)) return LOPA_ERR_INVALID;
   if (d->dtype != LOPA_BF16) return LOPA_ERR_UNSUPPORTED;
   const lopa::ModelShape s = lopa::model_shape(*d, *md);
-  if (s.hidden % 64 != 0 || s.inter % 64 != 0 || d->d % 2 != 0) return LOPA_ERR_UNSUPPORTED;
+  if (s.hidden % 64 != 0 || s.inter % 64 != 0 || d->d % 8 != 0) return LOPA_ERR_UNSUPPORTED;
   // every projection's weight and the embedding rows addressed by 32-bit offsets
   const long long kmax = s.inter > s.hidden ? s.inter : s.hidden;
   const long long nmax = 2LL * s.inter > s.qkv ? 2LL * s.inter : s.qkv;
   if (nmax * kmax * 2 >= (1LL << 31) || static_cast<long long>(s.M) * kmax * 2 >= (1LL << 31))
+    return LOPA_ERR_UNSUPPORTED;
+  // every projection's units fit the consumers' slot tables
+  const lopa::LayerGemms gm = lopa::layer_gemms(*d, *md);
+  if (gm.qkv.units > lopa::kSlotTableMax || gm.o.units > lopa::kSlotTableMax ||
+      gm.gu.units > lopa::kSlotTableMax || gm.down.units > lopa::kSlotTableMax)
     return LOPA_ERR_UNSUPPORTED;
   return LOPA_OK;
 }
@@ -334,6 +401,7 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
   unsigned short* ho = reinterpret_cast<unsigned short*>(w + wsl.ho);
   unsigned short* act = reinterpret_cast<unsigned short*>(w + wsl.act);
   float* P = reinterpret_cast<float*>(w + wsl.part);
+  float2* rope = reinterpret_cast<float2*>(w + wsl.rope);
   void* aws = w + wsl.attn;
   const size_t aws_bytes = wsl.total - wsl.attn;
   const int M = s.M;
@@ -342,8 +410,11 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
   const size_t kb_layer = static_cast<size_t>(M) * kv_rows_elems;   // elements
   const double log2_theta = log2(static_cast<double>(md->rope_theta));
   const int heads = dims->Hq + 2 * dims->Hkv;
-  const long long qkv_threads = static_cast<long long>(M) * heads * (dims->d / 2);
+  const long long qkv_threads = static_cast<long long>(M) * heads * (dims->d / 8);
 
+  const int nrope = dims->B * (dims->d / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((nrope + 255) / 256), dim3(256), 0, stream, dims->B,
+                     dims->L, dims->d, log2_theta, rope);
   hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(256), 0, stream, s.hidden, dims->V, md->mask_id,
                      md->rms_eps, br_tok, wt(lay.embed), wt(lay.layer0 + lay.attn_norm), x, h);
   LOPA_LAUNCH_CHECK();
@@ -354,8 +425,8 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
     // attention block
     if ((st = gemm_launch(gm.qkv, h, wt(lb + lay.wqkv), P, stream)) != LOPA_OK) return st;
     hipLaunchKernelGGL(k_qkv_epilogue, dim3(static_cast<unsigned>((qkv_threads + 255) / 256)),
-                       dim3(256), 0, stream, gm.qkv, P, dims->B, dims->L, dims->Hq, dims->Hkv,
-                       dims->d, log2_theta, wt(lb + lay.bqkv), q, kb, vb);
+                       dim3(256), 0, stream, gm.qkv, P, dims->B, dims->Hq, dims->Hkv, dims->d,
+                       rope, wt(lb + lay.bqkv), q, kb, vb);
     LOPA_LAUNCH_CHECK();
     const unsigned short* kp =
         dims->L > 0 ? static_cast<const unsigned short*>(Kp) + l * kp_layer : nullptr;
@@ -370,7 +441,7 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
     LOPA_LAUNCH_CHECK();
     // MLP block
     if ((st = gemm_launch(gm.gu, h, wt(lb + lay.wgu), P, stream)) != LOPA_OK) return st;
-    const long long na = static_cast<long long>(M) * s.inter;
+    const long long na = static_cast<long long>(M) * (s.inter / 4);
     hipLaunchKernelGGL(k_swiglu, dim3(static_cast<unsigned>((na + 255) / 256)), dim3(256), 0,
                        stream, gm.gu, P, s.inter, act);
     LOPA_LAUNCH_CHECK();

@@ -75,10 +75,11 @@ inline LayerGemms layer_gemms(const lopa_dims& d, const lopa_model_dims& md) {
 }
 
 // Workspace of lopa_branch_forward: residual stream x (float32), normed
-// activations h (bf16), Q, attention output, MLP activation (bf16), GEMM
-// partials and the attention call's own workspace.
+// activations h (bf16), Q, attention output, MLP activation (bf16), the
+// rotary table of the block's positions, GEMM partials and the attention
+// call's own workspace.
 struct ModelWorkspace {
-  size_t x, h, q, ho, act, part, attn, total;
+  size_t x, h, q, ho, act, rope, part, attn, total;
 };
 
 inline ModelWorkspace model_workspace(const lopa_dims& d, const lopa_model_dims& md) {
@@ -96,6 +97,7 @@ inline ModelWorkspace model_workspace(const lopa_dims& d, const lopa_model_dims&
   w.q = take(M * s.hq_d * 2);
   w.ho = take(M * s.hq_d * 2);
   w.act = take(M * s.inter * 2);
+  w.rope = take(static_cast<size_t>(d.B) * (d.d / 2) * 8);   // (cos, sin) float pairs
   w.part = take(layer_gemms(d, md).partial_bytes());
   w.attn = take(attn_workspace_bytes(d));
   w.total = at;

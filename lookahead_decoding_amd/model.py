@@ -62,9 +62,11 @@ class ForwardBuffers:
         self.ws = torch.zeros(model_workspace_bytes(dims, md), dtype=torch.uint8, device=device)
 
 
-def forward(model: Model, br_tok, nb, fb: ForwardBuffers, stream=None) -> None:
-    lopa_branch_forward(model.dims, model.md, model.weights, model.Kp, model.Vp, model.kv_rows,
-                        br_tok, nb, fb.Kb, fb.Vb, fb.H, fb.ws, stream)
+def forward(model: Model, br_tok, nb, fb: ForwardBuffers, stream=None, dims=None) -> None:
+    """``dims`` may differ from the model's in k_max (the weight layout does
+    not depend on it); ``fb`` must be sized for the dims used."""
+    lopa_branch_forward(model.dims if dims is None else dims, model.md, model.weights, model.Kp,
+                        model.Vp, model.kv_rows, br_tok, nb, fb.Kb, fb.Vb, fb.H, fb.ws, stream)
 
 
 def model_step(model: Model, k: int, tau: float, tok, conf, arg, buf, fb: ForwardBuffers,

@@ -115,6 +115,9 @@ FWD_CASES = [
     ("two-row-groups-M288", dict(L=64, B=32, k_max=8, Hq=4, Hkv=1, d=128, inter=1024, V=1500,
                                  n_layers=2), 9),
     ("no-prefix", dict(L=0, B=16, k_max=1, Hq=4, Hkv=4, d=64, inter=256, V=500, n_layers=2), 2),
+    # 144 rows: the 160-row projection tile with 16 padding rows
+    ("tile160-M144", dict(L=50, B=48, k_max=2, Hq=4, Hkv=2, d=64, inter=512, V=800,
+                          n_layers=2), 3),
 ]
 
 
