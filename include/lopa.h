@@ -119,6 +119,21 @@ int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
                       int32_t* rows, int32_t* row_ptr, hipStream_t stream);
 
 /*
+ * Explore with a branch count that follows the state: as lopa_branch_build,
+ * but only remaining positions with conf >= gamma are lookahead candidates,
+ * so k_eff = min(k, #{remaining p : conf[p] >= gamma}) and nb = 1 + k_eff.
+ * The blog's section 6 ("解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈")
+ * names branch counts that adapt to how hard the context is as a next step;
+ * this is one plain form of it: where the model is unsure of every other
+ * position, fewer speculative fills are verified.  gamma <= 0 gives
+ * lopa_branch_build exactly; NaN is rejected (LOPA_ERR_INVALID).
+ */
+int lopa_branch_build_floor(const lopa_dims* dims, int32_t k, float tau, float gamma,
+                            const int32_t* tok, const float* conf, const int32_t* arg,
+                            int32_t* nb, int32_t* br_tok, uint8_t* br_mask,
+                            int32_t* rows, int32_t* row_ptr, hipStream_t stream);
+
+/*
  * Verify, attention: for branch b < nb, position i < B, query head h with
  * key/value head g = h / (Hq/Hkv):
  *   H[b][i][h*d : h*d+d] = sum_j softmax_j(Q_b,i,h . K_j / sqrt(d)) V_j

@@ -80,6 +80,8 @@ _SIGS = {
     "lopa_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "lopa_branch_build": ([ctypes.POINTER(Dims), _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                           ctypes.c_int),
+    "lopa_branch_build_floor": ([ctypes.POINTER(Dims), _I, ctypes.c_float, ctypes.c_float] +
+                                [_P] * 9, ctypes.c_int),
     "lopa_branch_attn": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                          ctypes.c_int),
     "lopa_lmhead_conf": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -176,6 +178,17 @@ def lopa_branch_build(dims, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows, r
     i32, f32, u8 = torch.int32, torch.float32, torch.uint8
     _check("lopa_branch_build", lib().lopa_branch_build(
         ctypes.byref(dims), int(k), float(tau),
+        _ptr(tok, i32, "tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
+        _ptr(nb, i32, "nb"), _ptr(br_tok, i32, "br_tok"), _ptr(br_mask, u8, "br_mask"),
+        _ptr(rows, i32, "rows"), _ptr(row_ptr, i32, "row_ptr"), _stream(stream)))
+
+
+def lopa_branch_build_floor(dims, k, tau, gamma, tok, conf, arg, nb, br_tok, br_mask, rows,
+                            row_ptr, stream=None) -> None:
+    import torch
+    i32, f32, u8 = torch.int32, torch.float32, torch.uint8
+    _check("lopa_branch_build_floor", lib().lopa_branch_build_floor(
+        ctypes.byref(dims), int(k), float(tau), float(gamma),
         _ptr(tok, i32, "tok"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
         _ptr(nb, i32, "nb"), _ptr(br_tok, i32, "br_tok"), _ptr(br_mask, u8, "br_mask"),
         _ptr(rows, i32, "rows"), _ptr(row_ptr, i32, "row_ptr"), _stream(stream)))

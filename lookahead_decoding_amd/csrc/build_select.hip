@@ -16,7 +16,7 @@
 namespace lopa {
 
 __global__ void __launch_bounds__(64)
-k_branch_build(int B, int nb_max, int k, float tau,
+k_branch_build(int B, int nb_max, int k, float tau, float gamma,
                const int32_t* __restrict__ tok, const float* __restrict__ conf,
                const int32_t* __restrict__ arg, int32_t* __restrict__ nb_out,
                int32_t* __restrict__ br_tok, uint8_t* __restrict__ br_mask,
@@ -49,7 +49,11 @@ k_branch_build(int B, int nb_max, int k, float tau,
   // tau against at most tau, or the overall first), so among the remaining
   // positions the rank drops by the fill count
   rank -= n_fill;
-  const int k_eff = k < n_rem ? k : n_rem;
+  // lookahead candidates: the remaining positions whose confidence reaches
+  // the floor gamma (all of them for the plain call) -- a prefix of the
+  // remaining positions in rank order
+  const int n_cand = __popcll(__ballot(remaining && c >= gamma));
+  const int k_eff = k < n_cand ? k : n_cand;
   const int nb = 1 + k_eff;
   const int my_branch = (remaining && rank < k_eff) ? rank + 1 : 0;  // 0: not a lookahead pos
 
@@ -191,7 +195,23 @@ extern "C" int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
   if (!tok || !conf || !arg || !nb || !br_tok || !br_mask || !rows || !row_ptr)
     return LOPA_ERR_INVALID;
   hipLaunchKernelGGL(lopa::k_branch_build, dim3(1), dim3(64), 0, stream, dims->B,
-                     dims->k_max + 1, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows,
+                     dims->k_max + 1, k, tau, -INFINITY, tok, conf, arg, nb, br_tok, br_mask,
+                     rows, row_ptr);
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}
+
+extern "C" int lopa_branch_build_floor(const lopa_dims* dims, int32_t k, float tau, float gamma,
+                                       const int32_t* tok, const float* conf, const int32_t* arg,
+                                       int32_t* nb, int32_t* br_tok, uint8_t* br_mask,
+                                       int32_t* rows, int32_t* row_ptr, hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (k < 0 || k > dims->k_max || gamma != gamma) return LOPA_ERR_INVALID;
+  if (!tok || !conf || !arg || !nb || !br_tok || !br_mask || !rows || !row_ptr)
+    return LOPA_ERR_INVALID;
+  hipLaunchKernelGGL(lopa::k_branch_build, dim3(1), dim3(64), 0, stream, dims->B,
+                     dims->k_max + 1, k, tau, gamma, tok, conf, arg, nb, br_tok, br_mask, rows,
                      row_ptr);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;

@@ -20,7 +20,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_select,
+from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_build_floor,
+               lopa_branch_select,
                lopa_branch_select_alpha, lopa_lmhead_conf, lopa_lmhead_conf_ent,
                lopa_synth_qkv)
 from .step import StepBuffers
@@ -76,11 +77,16 @@ def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None) ->
 
 
 def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
-                alpha=None) -> None:
+                alpha=None, gamma=None) -> None:
     """One explore / verify / select step on the current state, then swap in
-    the winner's state."""
-    lopa_branch_build(dims, k, tau, buf.tok, buf.conf_s, buf.arg_s, buf.nb, buf.br_tok,
-                      buf.br_mask, buf.rows, buf.row_ptr, stream)
+    the winner's state.  ``gamma``: lookahead candidates need confidence >=
+    gamma (lopa_branch_build_floor)."""
+    if gamma is None:
+        lopa_branch_build(dims, k, tau, buf.tok, buf.conf_s, buf.arg_s, buf.nb, buf.br_tok,
+                          buf.br_mask, buf.rows, buf.row_ptr, stream)
+    else:
+        lopa_branch_build_floor(dims, k, tau, gamma, buf.tok, buf.conf_s, buf.arg_s, buf.nb,
+                                buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr, stream)
     lopa_synth_qkv(dims, seed, buf.br_tok, buf.nb, buf.Qb, buf.Kb, buf.Vb, stream)
     lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.nb, buf.H, buf.ws, stream)
     if alpha is None:
@@ -98,12 +104,12 @@ def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
 
 
 def decode_block(dims, k, tau, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, steps: int,
-                 log=None, stream=None, alpha=None) -> None:
+                 log=None, stream=None, alpha=None, gamma=None) -> None:
     """The initial pass and ``steps`` steps; ``log`` (device int32
     [steps][B]) receives the tokens after each step."""
     start_block(dims, seed, tok0, Kp, Vp, W, buf, stream)
     for s in range(steps):
-        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream, alpha)
+        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream, alpha, gamma)
         if log is not None:
             log[s].copy_(buf.tok)
 

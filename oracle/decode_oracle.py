@@ -178,16 +178,19 @@ def block_inputs(inp, seed: int, tokens: np.ndarray):
                    Kb=_pad(K, cfg.nb_max), Vb=_pad(V, cfg.nb_max))
 
 
-def _explore_gaps(tok, conf, tau, k):
+def _explore_gaps(tok, conf, tau, k, gamma=None):
     """Confidence gaps the explore stage's choices depend on: the threshold
-    test of every masked position, the fallback's top-1 against top-2 when
-    nothing passes it, and the order of the k+1 most confident positions
-    the anchor leaves (which of them the lookahead branches fill)."""
+    test of every masked position (and the candidate floor gamma, when
+    given), the fallback's top-1 against top-2 when nothing passes it, and
+    the order of the k+1 most confident positions the anchor leaves (which
+    of them the lookahead branches fill)."""
     m = np.flatnonzero(tok == MASK)
     if m.size == 0:
         return np.inf, np.inf
     c = conf.astype(np.float64)
     tau_gap = float(np.min(np.abs(c[m] - tau)))
+    if gamma is not None:
+        tau_gap = min(tau_gap, float(np.min(np.abs(c[m] - gamma))))
     above = [p for p in m if c[p] > tau]
     gaps = []
     order = sorted(m, key=lambda p: (-c[p], p))
@@ -203,7 +206,7 @@ def _explore_gaps(tok, conf, tau, k):
 
 
 def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = None,
-                 alpha: float | None = None) -> DecodeTrace:
+                 alpha: float | None = None, gamma: float | None = None) -> DecodeTrace:
     """Decode inp.tok's masked positions: the initial pass, then verification
     steps (explore, verify, select and reuse) until none is masked.  The
     committed prefix Kp, Vp and the weight W come from ``inp``; every
@@ -229,11 +232,13 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
     for _ in range(limit):
         if not np.any(tok == MASK):
             break
-        rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k)
+        g32 = None if gamma is None else np.float32(gamma)
+        rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k,
+                                          None if gamma is None else np.float64(g32))
         # explore with the state, then the projections of every branch's tokens
-        br = branch_build(tok, conf, arg, k, np.float32(tau), cfg.nb_max)
+        br = branch_build(tok, conf, arg, k, np.float32(tau), cfg.nb_max, g32)
         st = block_inputs(inp, seed, br.br_tok.reshape(cfg.nb_max, cfg.B)[:br.nb])
-        out = verification_step(replace(st, tok=tok), conf, arg, k, tau, alpha)
+        out = verification_step(replace(st, tok=tok), conf, arg, k, tau, alpha, gamma)
         sel = out.sel
         bc = np.sort(np.asarray(sel.bconf[:out.br.nb], np.float64))[::-1]
         win_margin = float(bc[0] - bc[1]) if bc.size > 1 else np.inf

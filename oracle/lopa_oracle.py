@@ -163,7 +163,8 @@ def anchor_fill_set(tok, conf, tau) -> list:
     return [best]
 
 
-def branch_build(tok, conf, arg, k: int, tau: float, nb_max: int) -> Branches:
+def branch_build(tok, conf, arg, k: int, tau: float, nb_max: int,
+                 gamma: float | None = None) -> Branches:
     """Anchor plus k lookahead branches, and the LM-head row list.
 
     Branch 0 (anchor) fills ``anchor_fill_set``.  The lookahead positions
@@ -174,6 +175,11 @@ def branch_build(tok, conf, arg, k: int, tau: float, nb_max: int) -> Branches:
 
     Branches b >= nb are written as copies of the anchor's tokens with no
     masked positions, and ``row_ptr[b+1] = M`` for them.
+
+    ``gamma`` (the branch count that follows the state, [blog] section 6's
+    adaptive branch count in one plain form): only remaining positions with
+    confidence >= gamma are lookahead candidates, k_eff = min(k, their
+    number); None keeps every remaining position.
     """
     tok = np.asarray(tok, dtype=np.int32)
     B = len(tok)
@@ -183,7 +189,9 @@ def branch_build(tok, conf, arg, k: int, tau: float, nb_max: int) -> Branches:
     masked = [p for p in range(B) if tok[p] == MASK]
     remaining = [p for p in masked if p not in fill]
     ranked = sorted(remaining, key=lambda p: (-float(conf[p]), p))
-    k_eff = min(k, len(remaining))
+    if gamma is not None:
+        ranked = [p for p in ranked if float(conf[p]) >= float(gamma)]
+    k_eff = min(k, len(ranked))
     look = ranked[:k_eff]
     nb = 1 + k_eff
 
@@ -411,15 +419,18 @@ def initial_state(inp) -> tuple[np.ndarray, np.ndarray, HeadOut]:
 
 
 def verification_step(inp, conf, arg, k: int | None = None,
-                      tau: float | None = None, alpha: float | None = None) -> StepOut:
+                      tau: float | None = None, alpha: float | None = None,
+                      gamma: float | None = None) -> StepOut:
     """One LoPA iteration: explore, verify (attention + LM head) and select.
 
     ``conf`` must be float32 (the library's input precision).  ``alpha``
-    selects with ``branch_select_alpha`` instead of the mean confidence."""
+    selects with ``branch_select_alpha`` instead of the mean confidence;
+    ``gamma`` is branch_build's confidence floor for lookahead candidates."""
     cfg = inp.cfg
     k = cfg.k if k is None else k
     tau = cfg.tau if tau is None else tau
-    br = branch_build(inp.tok, conf, arg, k, np.float32(tau), cfg.nb_max)
+    br = branch_build(inp.tok, conf, arg, k, np.float32(tau), cfg.nb_max,
+                      None if gamma is None else np.float32(gamma))
     H = branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, br.nb, cfg.Hq, cfg.Hkv)
     H = round_like(H, inp.Qb.dtype)
     Hrows = np.stack([H[r // cfg.B, r % cfg.B] for r in br.rows]) if len(br.rows) \
