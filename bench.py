@@ -87,7 +87,7 @@ def algorithmic(cfg, nb: int, M: int) -> dict:
 
 
 def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10, alpha=None,
-                   gamma=None) -> dict:
+                   gamma=None, temperature=None) -> dict:
     """Decode the workload's block (its masked positions) from the initial
     pass until none is masked, with token-keyed projections: steps, tokens per
     step (TPF), and the time of the whole block (initial pass + its steps).
@@ -107,22 +107,21 @@ def decode_measure(dims, cfg, inp, x, k: int, seed: int, reps: int = 10, alpha=N
         start_block(dims, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf)
         c = buf.conf_s.cpu().numpy()[np.asarray(inp.tok) == MASK]
         gamma = float(np.median(c)) if c.size else 0.0
-    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log,
-                 alpha=alpha, gamma=gamma)
+    opts = dict(alpha=alpha, gamma=gamma, temperature=temperature, sample_seed=seed)
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log, **opts)
     torch.cuda.synchronize()
     got = log.cpu().numpy()
     done = [s for s in range(m) if not np.any(got[s] == MASK)]
     steps = done[0] + 1 if done else m
-    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps,
-                 alpha=alpha, gamma=gamma)
+    decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps, **opts)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
-        decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps,
-                     alpha=alpha, gamma=gamma)
+        decode_block(dims, k, cfg.tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, steps, **opts)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / reps * 1e3
-    return {"k": k, "alpha": alpha, "gamma": gamma, "masked": m, "steps": steps, "tpf": round(m / steps, 3),
+    return {"k": k, "alpha": alpha, "gamma": gamma, "temperature": temperature, "masked": m,
+            "steps": steps, "tpf": round(m / steps, 3),
             "ms_per_block": round(ms, 3), "decoded_tokens_per_s": round(m / (ms * 1e-3), 1)}
 
 
@@ -342,7 +341,7 @@ def main():
     per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
     call_us = per.mean(axis=0) * 1e3
     # the entropy-carrying LM head and the alternative select on the same rows
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for i in range(K):
         e = ev2[i]
         e[0].record(stream)
@@ -353,8 +352,11 @@ def main():
                                       buf.br_tok, buf.conf, buf.arg, buf.ent, buf.bconf,
                                       buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
         e[2].record(stream)
+        lopa.lopa_lmhead_sample(dims, 0.9, 1000 + i, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb,
+                                buf.conf, buf.arg, None, buf.ws)
+        e[3].record(stream)
     torch.cuda.synchronize()
-    alt_us = np.array([[ev2[i][j].elapsed_time(ev2[i][j + 1]) for j in range(2)]
+    alt_us = np.array([[ev2[i][j].elapsed_time(ev2[i][j + 1]) for j in range(3)]
                        for i in range(K)]).mean(axis=0) * 1e3
     # the roofline uses the LM-head call timed inside the timed loop (eager), else the
     # separate per-call loop (graph replay has no per-call events)
@@ -391,7 +393,8 @@ def main():
                     "lmhead_conf": round(float(call_us[2]), 2),
                     "branch_select": round(float(call_us[3]), 2),
                     "lmhead_conf_ent": round(float(alt_us[0]), 2),
-                    "branch_select_alpha": round(float(alt_us[1]), 2)},
+                    "branch_select_alpha": round(float(alt_us[1]), 2),
+                    "lmhead_sample": round(float(alt_us[2]), 2)},
         "roofline": {"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -417,6 +420,8 @@ def main():
             "lookahead_alpha_0.5": decode_measure(dims, cfg, inp, x, cfg.k, seed, alpha=0.5),
             "lookahead_floor_median": decode_measure(dims, cfg, inp, x, cfg.k, seed,
                                                      gamma="median"),
+            "lookahead_sampled_T0.9": decode_measure(dims, cfg, inp, x, cfg.k, seed,
+                                                     temperature=0.9),
         }
     if not args.no_model and cfg.dtype == "bf16":
         out["model_step"] = model_measure(cfg, inp, args.model_steps, 5)

@@ -195,6 +195,26 @@ int lopa_lmhead_conf_ent(const lopa_dims* dims, const void* H, const void* W,
                          hipStream_t stream);
 
 /*
+ * lopa_lmhead_conf with temperature sampling in place of the argmax
+ * ("解码效率革命：LoPA如何突破扩散语言模型的并行瓶颈", section 5: a temperature of
+ * 0.7-1.1 rather than greedy decoding).  For every listed row r at block
+ * position p = r mod B:
+ *   arg[r]  = argmax_v ( l_v / T + G_v ),  G_v = -ln(-ln u_v)  (Gumbel-max: a
+ *             draw from softmax(l / T); lowest v on a tie)
+ *   conf[r] = softmax(l / T)[arg[r]]
+ * with u_v = (2 (x >> 9) + 1) 2^-24, x = word v % 4 of Philox4x32-10 (Salmon
+ * et al., SC 2011) under key (seed low 32 bits, seed high 32 bits) and
+ * counter (v / 4, p, 0x5AB1E, 0): the noise depends on the position, not the
+ * branch.  Same single streaming pass as lopa_lmhead_conf.
+ * In  temperature > 0 and finite (else LOPA_ERR_INVALID); seed (a new one
+ *     per pass for independent draws); the rest as lopa_lmhead_conf.
+ */
+int lopa_lmhead_sample(const lopa_dims* dims, float temperature, uint64_t seed,
+                       const void* H, const void* W, const int32_t* rows,
+                       const int32_t* row_ptr, const int32_t* nb, float* conf, int32_t* arg,
+                       float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Select and reuse: branch confidence bconf[b] = mean of conf[b*B+p] over
  * the p with br_mask[b*B+p] = 1 (1.0 when there is none), for b < nb;
  * bconf[b] = -1 for b >= nb.  winner = the first b with the largest bconf

@@ -92,6 +92,8 @@ _SIGS = {
                               ctypes.c_size_t, _P], ctypes.c_int),
     "lopa_branch_select_alpha": ([ctypes.POINTER(Dims), ctypes.c_float] + [_P] * 14,
                                  ctypes.c_int),
+    "lopa_lmhead_sample": ([ctypes.POINTER(Dims), ctypes.c_float, ctypes.c_uint64] + [_P] * 9 +
+                           [ctypes.c_size_t, _P], ctypes.c_int),
     "lopa_synth_qkv": ([ctypes.POINTER(Dims), ctypes.c_uint64, _P, _P, _P, _P, _P, _P],
                        ctypes.c_int),
     "lopa_commit_block": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _I, _P], ctypes.c_int),
@@ -241,6 +243,19 @@ def lopa_lmhead_conf_ent(dims, H, W, rows, row_ptr, nb, conf, arg, ent, logits_o
         _ptr(arg, i32, "arg"), _ptr(ent, f32, "ent"), _ptr(logits_out, f32, "logits_out"),
         _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def lopa_lmhead_sample(dims, temperature, seed, H, W, rows, row_ptr, nb, conf, arg, logits_out,
+                       ws, stream=None) -> None:
+    import torch
+    a = _act_dtype(dims)
+    i32, f32 = torch.int32, torch.float32
+    _check("lopa_lmhead_sample", lib().lopa_lmhead_sample(
+        ctypes.byref(dims), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(H, a, "H"),
+        _ptr(W, a, "W"), _ptr(rows, i32, "rows"), _ptr(row_ptr, i32, "row_ptr"),
+        _ptr(nb, i32, "nb"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
+        _ptr(logits_out, f32, "logits_out"), _ptr(ws, None, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def lopa_branch_select_alpha(dims, alpha, tok, conf_state, nb, br_mask, br_tok, conf, arg, ent,

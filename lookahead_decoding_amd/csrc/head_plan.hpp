@@ -70,10 +70,11 @@ __host__ __device__ inline HeadGroups head_groups(int M) {
 }
 
 // Per (row, vocabulary tile) partial: max logit (float), scaled sum (float),
-// argmax (int32), entropy term (float) -- four planes of m_max * ntiles.
+// argmax or sample (int32), entropy term or perturbed best score (float),
+// scaled logit of the sample (float) -- five planes of m_max * ntiles.
 inline size_t lmhead_workspace_bytes(const lopa_dims& d) {
   const HeadPlan p = head_plan(d);
-  return static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 16u;
+  return static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 20u;
 }
 
 }  // namespace lopa

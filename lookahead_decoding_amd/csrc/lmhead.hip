@@ -25,9 +25,12 @@
 //                   through L2.
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
+#include <type_traits>
+
 #include "lopa_common.hpp"
 #include "head_plan.hpp"
 #include "stream_tile.hpp"
+#include "philox.hpp"
 
 namespace lopa {
 
@@ -35,6 +38,78 @@ namespace lopa {
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
+
+// What the LM head folds per row: the confidence and argmax; also the
+// entropy term; or, for temperature sampling, the scaled-logit softmax and a
+// Gumbel-max sample.
+constexpr int kModeConf = 0, kModeEnt = 1, kModeSample = 2;
+
+// Temperature sampling: scaled logits z = l / T, Gumbel noise from Philox4x32-10
+// with key (seed low, seed high) and counter (v / 4, block position, kSampleTag,
+// 0), word v % 4 -> u = (2 (x >> 9) + 1) 2^-24 (exact, in (0, 1)),
+// G = -ln(-ln u).  The sample is the argmax of z + G (Gumbel-max: a draw
+// from softmax(z)); the noise depends on the position, not the branch, so
+// branches holding the same logits at a position draw the same token.
+constexpr unsigned kSampleTag = 0x5AB1Eu;
+struct Sampling {
+  float inv_t;
+  unsigned k0, k1;
+  int B;
+};
+
+__device__ __forceinline__ float gumbel(unsigned x) {
+  const float u = static_cast<float>(2u * (x >> 9) + 1u) * (1.f / 16777216.f);
+  return -logf(-logf(u));
+}
+
+// Sampling partial of one lane's logits for one LM-head row at block
+// position pos (layout as row_partial below), merged with the other lane
+// half that holds the same row.
+template <int NV>
+__device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], int vb, int h,
+                                                       int vend, const Sampling& smp,
+                                                       unsigned pos) {
+  SPartial p = empty_spartial();
+#pragma unroll
+  for (int n = 0; n < NV; ++n)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int v0 = vb + n * 32 + 8 * q4 + 4 * h;   // a multiple of 4
+      unsigned key0 = smp.k0, key1 = smp.k1;
+      // the key schedule in vector registers: hoisted into scalar registers
+      // for every call at once, it spills
+      __asm__ volatile("" : "+v"(key0), "+v"(key1));
+      const U32x4 w = philox4x32_10(
+          U32x4{static_cast<unsigned>(v0) >> 2, pos, kSampleTag, 0u}, key0, key1);
+      const unsigned xs[4] = {w.x0, w.x1, w.x2, w.x3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = v0 + j;
+        if (v < vend) {
+          const float z = a[n][4 * q4 + j] * smp.inv_t;
+          p.m = fmaxf(p.m, z);
+          const float gv = z + gumbel(xs[j]);
+          if (gv > p.g) {   // v ascends within the lane: the lowest v keeps a tie
+            p.g = gv;
+            p.i = v;
+            p.z = z;
+          }
+        }
+      }
+    }
+  if (p.i != 0x7fffffff) {
+    float s = 0.f;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vb + n * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (v < vend) s += exp2f((a[n][r] * smp.inv_t - p.m) * kLog2e);
+      }
+    p.s = s;
+  }
+  return merge(p, shfl_xor(p, 32));
+}
 
 // Online-softmax partial of one lane's logits for one LM-head row:
 // a[n][r] = logit of vocabulary entry vb + 32n + 8(r/4) + 4h + r%4 (the
@@ -76,7 +151,7 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
 constexpr int kRunRows = 512;    // running partials: compute-wave columns x rows
 constexpr int kHeadThreads = kStreamThreads;
 constexpr int kHeadStage = (256 + 128) * kRB;        // largest BUF of the bodies below
-constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(sizeof(Partial));
+constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(sizeof(SPartial));
 
 // One persistent workgroup owns a contiguous, balanced vocabulary range
 // (multiples of 16 rows) of its part and the Mg rows of its row group; it
@@ -99,7 +174,7 @@ constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(siz
 // the workgroup's range, so loads past it return zeros without touching
 // memory.  Chunks are visited in an order rotated by the part, so the
 // compute units of one XCD do not all ask for the same H lines at once.
-template <int WX, int NVW, int MTW, bool ENT>
+template <int WX, int NVW, int MTW, int MODE>
 __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int part, int Mg,
                                           int row0, int h_bytes,
                                           const unsigned short* __restrict__ H,
@@ -107,7 +182,10 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
                                           const int32_t* __restrict__ rows, unsigned char* smem,
                                           float* __restrict__ ws_m, float* __restrict__ ws_s,
                                           int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
+                                          float* __restrict__ ws_z, const Sampling smp,
                                           float* __restrict__ logits_out) {
+  constexpr bool ENT = MODE == kModeEnt;
+  using RP = typename std::conditional<MODE == kModeSample, SPartial, Partial>::type;
   using T = StreamTile<WX, NVW, MTW>;
   constexpr int WROWS = T::WROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
   constexpr int RUNS = kRunRows / WX;   // running-partial stride per wave column
@@ -126,8 +204,11 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   const int total = npass * nch;
   const int rot = ((part >> 3) * nch / 32) % nch;
 
-  Partial* run = reinterpret_cast<Partial*>(smem + kStages * kHeadStage);
-  for (int r = tid; r < kRunRows; r += kHeadThreads) run[r] = empty_partial();
+  RP* run = reinterpret_cast<RP*>(smem + kStages * kHeadStage);
+  for (int r = tid; r < kRunRows; r += kHeadThreads) {
+    if constexpr (MODE == kModeSample) run[r] = empty_spartial();
+    else run[r] = empty_partial();
+  }
   __syncthreads();
 
   if (w >= kComputeWaves) {
@@ -223,11 +304,17 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
       const int vbw = v_lo + pass * WROWS + wx * (32 * NVW);
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
-        const Partial p = row_partial<NVW, ENT>(acc[mt], vbw, lh, v_hi);
         const int r = (wy * MTW + mt) * 32 + ln;
+        RP p;
+        if constexpr (MODE == kModeSample) {
+          const unsigned pos = static_cast<unsigned>(rows[row0 + min(r, Mg - 1)] % smp.B);
+          p = row_partial_sample<NVW>(acc[mt], vbw, lh, v_hi, smp, pos);
+        } else {
+          p = row_partial<NVW, ENT>(acc[mt], vbw, lh, v_hi);
+        }
         if (lh == 0) {
-          Partial q = merge(run[wx * RUNS + r], p);
-          if constexpr (!ENT) q.t = 0.f;   // keeps the entropy arithmetic out
+          RP q = merge(run[wx * RUNS + r], p);
+          if constexpr (MODE == kModeConf) q.t = 0.f;   // keeps the entropy arithmetic out
           run[wx * RUNS + r] = q;
         }
         if (logits_out && r < Mg) {
@@ -252,7 +339,7 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   }
   __syncthreads();
   for (int r = tid; r < Mg; r += kHeadThreads) {
-    Partial p = run[r];
+    RP p = run[r];
 #pragma unroll
     for (int x = 1; x < WX; ++x) p = merge(p, run[x * RUNS + r]);
     const size_t o = static_cast<size_t>(row0 + r) * nparts + part;
@@ -260,6 +347,10 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     ws_s[o] = p.s;
     ws_i[o] = p.i;
     if constexpr (ENT) ws_t[o] = p.t;
+    if constexpr (MODE == kModeSample) {
+      ws_t[o] = p.g;
+      ws_z[o] = p.z;
+    }
   }
 }
 
@@ -267,15 +358,16 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
 // on XCD b % 8; the row groups of one vocabulary part take consecutive
 // blocks of the same XCD, so they stream the same weight lines together and
 // the second reader is served from that XCD's L2 (or the MALL behind it).
-// ENT: the partials also carry the entropy term.
-template <bool ENT>
+// MODE: conf only, + entropy term, or temperature sampling (ws_t then
+// holds the perturbed best score, ws_z the scaled logit of the sample).
+template <int MODE>
 __global__ void __launch_bounds__(kHeadThreads)
 k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
               const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
               float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
-              float* __restrict__ logits_out) {
+              float* __restrict__ ws_z, const Sampling smp, float* __restrict__ logits_out) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHeadSmem];
   const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
   if (M <= 0) return;
@@ -288,14 +380,14 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
   if (part >= g.nparts || row0 >= M) return;
   const int Mg = min(M - row0, g.tpg * 32);
 #define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
-                  ws_t, logits_out
+                  ws_t, ws_z, smp, logits_out
   // up to 4 tiles: 4 x 2 compute waves (256 vocabulary rows per pass);
   // 5..8 tiles: 2 x 4 compute waves (128 vocabulary rows per pass)
   if (!g.wide) {
-    if (g.tpg <= 2) head_body<4, 2, 1, ENT>(LOPA_ARGS);
-    else head_body<4, 2, 2, ENT>(LOPA_ARGS);
+    if (g.tpg <= 2) head_body<4, 2, 1, MODE>(LOPA_ARGS);
+    else head_body<4, 2, 2, MODE>(LOPA_ARGS);
   } else {
-    head_body<2, 2, 2, ENT>(LOPA_ARGS);
+    head_body<2, 2, 2, MODE>(LOPA_ARGS);
   }
 #undef LOPA_ARGS
 }
@@ -304,27 +396,39 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
 // Plain path
 // ---------------------------------------------------------------------------
 
-template <typename T>
+template <typename T, int MODE>
 __global__ void __launch_bounds__(256)
 k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __restrict__ H,
                const T* __restrict__ W,
                const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
                const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
                float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
-               float* __restrict__ logits_out) {
-  __shared__ Partial red[4];
+               float* __restrict__ ws_z, const Sampling smp, float* __restrict__ logits_out) {
+  using RP = typename std::conditional<MODE == kModeSample, SPartial, Partial>::type;
+  __shared__ RP red[4];
   const int m = blockIdx.y;
   const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
   if (m >= M) return;
   const int row = rows[m];
   const int v = blockIdx.x * kPlainVocabPerWG + threadIdx.x;
-  Partial p = empty_partial();
+  RP p;
+  if constexpr (MODE == kModeSample) p = empty_spartial();
+  else p = empty_partial();
   if (v < V) {
     float l = 0.f;
     const size_t hb = static_cast<size_t>(row) * hidden;
     const size_t wb = static_cast<size_t>(v) * hidden;
     for (int k = 0; k < hidden; ++k) l = fmaf(Act<T>::load(H, hb + k), Act<T>::load(W, wb + k), l);
-    p = Partial{l, 1.f, v, 0.f};
+    if constexpr (MODE == kModeSample) {
+      const U32x4 w = philox4x32_10(
+          U32x4{static_cast<unsigned>(v) >> 2, static_cast<unsigned>(row % smp.B), kSampleTag, 0u},
+          smp.k0, smp.k1);
+      const unsigned xs[4] = {w.x0, w.x1, w.x2, w.x3};
+      const float z = l * smp.inv_t;
+      p = SPartial{z, 1.f, v, z + gumbel(xs[v & 3]), z};
+    } else {
+      p = Partial{l, 1.f, v, 0.f};
+    }
     if (logits_out) logits_out[static_cast<size_t>(row) * V + v] = l;
   }
 #pragma unroll
@@ -337,33 +441,47 @@ k_lmhead_plain(int V, int hidden, int ntiles, int nb_max, int m_max, const T* __
     ws_m[o] = p.m;
     ws_s[o] = p.s;
     ws_i[o] = p.i;
-    if (ws_t) ws_t[o] = p.t;
+    if constexpr (MODE == kModeEnt) ws_t[o] = p.t;
+    if constexpr (MODE == kModeSample) {
+      ws_t[o] = p.g;
+      ws_z[o] = p.z;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the vocabulary tiles of each row: conf = 1 / sum, arg = argmax,
-// and where ent is given the entropy of the row's softmax divided by ln V
-// (0 when V == 1).
+// Merge of the vocabulary tiles of each row: conf = 1 / sum, arg = argmax;
+// with the entropy, ent = the entropy of the row's softmax divided by ln V
+// (0 when V == 1); when sampling, conf = the sampled token's probability
+// under softmax(l / T) and arg = the sample.
 // ---------------------------------------------------------------------------
 
+template <int MODE>
 __global__ void __launch_bounds__(256)
 k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
                const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
                const int32_t* __restrict__ nb_ptr, const float* __restrict__ ws_m,
                const float* __restrict__ ws_s, const int32_t* __restrict__ ws_i,
-               const float* __restrict__ ws_t, float* __restrict__ conf,
-               int32_t* __restrict__ arg, float* __restrict__ ent) {
-  __shared__ Partial red[4];
+               const float* __restrict__ ws_t, const float* __restrict__ ws_z,
+               float* __restrict__ conf, int32_t* __restrict__ arg, float* __restrict__ ent) {
+  using RP = typename std::conditional<MODE == kModeSample, SPartial, Partial>::type;
+  __shared__ RP red[4];
   const int m = blockIdx.x;
   const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
   if (m >= M) return;
   if (mfma) ntiles = head_groups(M).nparts;
-  Partial p = empty_partial();
+  RP p;
+  if constexpr (MODE == kModeSample) p = empty_spartial();
+  else p = empty_partial();
   const size_t base = static_cast<size_t>(m) * ntiles;
-  for (int t = threadIdx.x; t < ntiles; t += 256)
-    p = merge(p, Partial{ws_m[base + t], ws_s[base + t], ws_i[base + t],
-                         ent ? ws_t[base + t] : 0.f});
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    if constexpr (MODE == kModeSample)
+      p = merge(p, SPartial{ws_m[base + t], ws_s[base + t], ws_i[base + t], ws_t[base + t],
+                            ws_z[base + t]});
+    else
+      p = merge(p, Partial{ws_m[base + t], ws_s[base + t], ws_i[base + t],
+                           MODE == kModeEnt ? ws_t[base + t] : 0.f});
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) p = merge(p, shfl_xor(p, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
@@ -371,19 +489,27 @@ k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
   if (threadIdx.x == 0) {
     p = merge(merge(red[0], red[1]), merge(red[2], red[3]));
     const int r = rows[m];
-    conf[r] = 1.f / p.s;
     arg[r] = p.i;
-    if (ent) ent[r] = V > 1 ? (logf(p.s) - p.t / p.s) / logf(static_cast<float>(V)) : 0.f;
+    if constexpr (MODE == kModeSample) {
+      conf[r] = exp2f((p.z - p.m) * kLog2e) / p.s;
+    } else {
+      conf[r] = 1.f / p.s;
+      if constexpr (MODE == kModeEnt)
+        ent[r] = V > 1 ? (logf(p.s) - p.t / p.s) / logf(static_cast<float>(V)) : 0.f;
+    }
   }
 }
 
 }  // namespace lopa
 
-// Both entry points: ent == nullptr leaves the entropy out.
+// All three entry points.  Workspace planes of m_max x ntiles: max, sum,
+// index, then the entropy term or the perturbed best score, then the scaled
+// logit of the sample.
+template <int MODE>
 static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
                          const int32_t* rows, const int32_t* row_ptr, const int32_t* nb,
-                         float* conf, int32_t* arg, float* ent, float* logits_out, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         float* conf, int32_t* arg, float* ent, const lopa::Sampling& smp,
+                         float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   using namespace lopa;
   int st = lopa_check_dims(dims);
   if (st != LOPA_OK) return st;
@@ -396,38 +522,34 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
   float* wm = static_cast<float*>(ws);
   float* wsum = wm + plane;
   int32_t* wi = reinterpret_cast<int32_t*>(wsum + plane);
-  float* wt = ent ? reinterpret_cast<float*>(wi + plane) : nullptr;
+  float* wt = reinterpret_cast<float*>(wi + plane);
+  float* wz = wt + plane;
   const int V = dims->V;
   const int nb_max = dims->k_max + 1;
   const unsigned short* Hb = static_cast<const unsigned short*>(H);
   const unsigned short* Wb = static_cast<const unsigned short*>(W);
   const int h_bytes = p.m_max * hidden * 2;   // H is [nb_max][B][hidden]
   if (p.mfma) {
-    if (ent)
-      hipLaunchKernelGGL(k_lmhead_mfma<true>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V,
-                         hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum,
-                         wi, wt, logits_out);
-    else
-      hipLaunchKernelGGL(k_lmhead_mfma<false>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream,
-                         V, hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum,
-                         wi, wt, logits_out);
+    hipLaunchKernelGGL(k_lmhead_mfma<MODE>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V,
+                       hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi,
+                       wt, wz, smp, logits_out);
   } else {
     const dim3 grid(p.ntiles, p.m_max);
     if (dims->dtype == LOPA_F32) {
-      hipLaunchKernelGGL(k_lmhead_plain<float>, grid, dim3(256), 0, stream, V, hidden, p.ntiles,
-                         nb_max, p.m_max, static_cast<const float*>(H),
-                         static_cast<const float*>(W), rows, row_ptr, nb, wm, wsum, wi, wt,
-                         logits_out);
+      hipLaunchKernelGGL((k_lmhead_plain<float, MODE>), grid, dim3(256), 0, stream, V, hidden,
+                         p.ntiles, nb_max, p.m_max, static_cast<const float*>(H),
+                         static_cast<const float*>(W), rows, row_ptr, nb, wm, wsum, wi, wt, wz,
+                         smp, logits_out);
     } else {
-      hipLaunchKernelGGL(k_lmhead_plain<unsigned short>, grid, dim3(256), 0, stream, V, hidden,
-                         p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi, wt,
-                         logits_out);
+      hipLaunchKernelGGL((k_lmhead_plain<unsigned short, MODE>), grid, dim3(256), 0, stream, V,
+                         hidden, p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum,
+                         wi, wt, wz, smp, logits_out);
     }
   }
   LOPA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_lmhead_merge, dim3(p.m_max), dim3(256), 0, stream, V, p.ntiles,
-                     p.mfma ? 1 : 0, nb_max, p.m_max, rows, row_ptr, nb, wm, wsum, wi, wt, conf,
-                     arg, ent);
+  hipLaunchKernelGGL(k_lmhead_merge<MODE>, dim3(p.m_max), dim3(256), 0, stream, V, p.ntiles,
+                     p.mfma ? 1 : 0, nb_max, p.m_max, rows, row_ptr, nb, wm, wsum, wi, wt, wz,
+                     conf, arg, ent);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;
 }
@@ -437,8 +559,8 @@ extern "C" int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void
                                 const int32_t* nb, float* conf, int32_t* arg,
                                 float* logits_out, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  return lmhead_launch(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr, logits_out, ws,
-                       ws_bytes, stream);
+  return lmhead_launch<lopa::kModeConf>(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr,
+                                        lopa::Sampling{}, logits_out, ws, ws_bytes, stream);
 }
 
 extern "C" int lopa_lmhead_conf_ent(const lopa_dims* dims, const void* H, const void* W,
@@ -447,6 +569,18 @@ extern "C" int lopa_lmhead_conf_ent(const lopa_dims* dims, const void* H, const 
                                     float* logits_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream) {
   if (!ent) return LOPA_ERR_INVALID;
-  return lmhead_launch(dims, H, W, rows, row_ptr, nb, conf, arg, ent, logits_out, ws, ws_bytes,
-                       stream);
+  return lmhead_launch<lopa::kModeEnt>(dims, H, W, rows, row_ptr, nb, conf, arg, ent,
+                                       lopa::Sampling{}, logits_out, ws, ws_bytes, stream);
+}
+
+extern "C" int lopa_lmhead_sample(const lopa_dims* dims, float temperature, uint64_t seed,
+                                  const void* H, const void* W, const int32_t* rows,
+                                  const int32_t* row_ptr, const int32_t* nb, float* conf,
+                                  int32_t* arg, float* logits_out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return LOPA_ERR_INVALID;
+  const lopa::Sampling smp{1.f / temperature, static_cast<unsigned>(seed),
+                           static_cast<unsigned>(seed >> 32), dims ? dims->B : 1};
+  return lmhead_launch<lopa::kModeSample>(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr, smp,
+                                          logits_out, ws, ws_bytes, stream);
 }

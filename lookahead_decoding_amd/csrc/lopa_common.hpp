@@ -101,6 +101,35 @@ __device__ __forceinline__ Partial merge(Partial a, Partial b) {
   return r;
 }
 
+// Partial of the sampling LM head over the scaled logits z = l / T: m = max
+// z, s = sum exp(z - m); (g, i, z_i) = the largest perturbed score z + G
+// (Gumbel noise G), its index (lowest on a tie) and the scaled logit there.
+// The empty partial has s == 0.
+struct SPartial {
+  float m;
+  float s;
+  int i;
+  float g;
+  float z;
+};
+
+__device__ __forceinline__ SPartial empty_spartial() {
+  return SPartial{-INFINITY, 0.f, 0x7fffffff, -INFINITY, 0.f};
+}
+
+__device__ __forceinline__ SPartial merge(SPartial a, SPartial b) {
+  if (b.s == 0.f) return a;
+  if (a.s == 0.f) return b;
+  SPartial r;
+  r.m = fmaxf(a.m, b.m);
+  r.s = a.s * exp2f((a.m - r.m) * kLog2e) + b.s * exp2f((b.m - r.m) * kLog2e);
+  const bool tb = better(b.g, b.i, a.g, a.i);
+  r.g = tb ? b.g : a.g;
+  r.i = tb ? b.i : a.i;
+  r.z = tb ? b.z : a.z;
+  return r;
+}
+
 // Rows listed for the LM head, from the device-side branch count; both are
 // clamped to the sizes the launch was planned for.
 __device__ __forceinline__ int listed_rows(const int32_t* row_ptr, const int32_t* nb_ptr,
@@ -109,6 +138,16 @@ __device__ __forceinline__ int listed_rows(const int32_t* row_ptr, const int32_t
   nb = nb < 0 ? 0 : (nb > nb_max ? nb_max : nb);
   const int M = row_ptr[nb];
   return M < 0 ? 0 : (M > m_max ? m_max : M);
+}
+
+__device__ __forceinline__ SPartial shfl_xor(SPartial p, int o) {
+  SPartial q;
+  q.m = __shfl_xor(p.m, o, kWave);
+  q.s = __shfl_xor(p.s, o, kWave);
+  q.i = __shfl_xor(p.i, o, kWave);
+  q.g = __shfl_xor(p.g, o, kWave);
+  q.z = __shfl_xor(p.z, o, kWave);
+  return q;
 }
 
 __device__ __forceinline__ Partial shfl_xor(Partial p, int o) {

@@ -23,7 +23,7 @@ import numpy as np
 from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_build_floor,
                lopa_branch_select,
                lopa_branch_select_alpha, lopa_lmhead_conf, lopa_lmhead_conf_ent,
-               lopa_synth_qkv)
+               lopa_lmhead_sample, lopa_synth_qkv)
 from .step import StepBuffers
 
 
@@ -52,7 +52,8 @@ class DecodeBuffers(StepBuffers):
         self.arg_s, self.arg_next = self.arg_next, self.arg_s
 
 
-def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None) -> None:
+def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None,
+                temperature=None, sample_seed=0) -> None:
     """Load the block ``tok0`` (host int32 [B], MASK where masked) and run the
     initial pass: slot 0's projections, attention, and the LM head on every
     masked position, which gives the state the first step starts from."""
@@ -70,14 +71,18 @@ def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None) ->
     lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.one, buf.H, buf.ws, stream)
     buf.conf.zero_()
     buf.arg.fill_(-1)
-    lopa_lmhead_conf(dims, buf.H, W, buf.rows0, buf.row_ptr0, buf.one, buf.conf, buf.arg, None,
-                     buf.ws, stream)
+    if temperature is None:
+        lopa_lmhead_conf(dims, buf.H, W, buf.rows0, buf.row_ptr0, buf.one, buf.conf, buf.arg,
+                         None, buf.ws, stream)
+    else:
+        lopa_lmhead_sample(dims, temperature, sample_seed, buf.H, W, buf.rows0, buf.row_ptr0,
+                           buf.one, buf.conf, buf.arg, None, buf.ws, stream)
     buf.conf_s.copy_(buf.conf[:B])
     buf.arg_s.copy_(buf.arg[:B])
 
 
 def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
-                alpha=None, gamma=None) -> None:
+                alpha=None, gamma=None, temperature=None, sample_seed=0) -> None:
     """One explore / verify / select step on the current state, then swap in
     the winner's state.  ``gamma``: lookahead candidates need confidence >=
     gamma (lopa_branch_build_floor)."""
@@ -89,7 +94,12 @@ def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
                                 buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr, stream)
     lopa_synth_qkv(dims, seed, buf.br_tok, buf.nb, buf.Qb, buf.Kb, buf.Vb, stream)
     lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.nb, buf.H, buf.ws, stream)
-    if alpha is None:
+    if temperature is not None:
+        lopa_lmhead_sample(dims, temperature, sample_seed, buf.H, W, buf.rows, buf.row_ptr,
+                           buf.nb, buf.conf, buf.arg, None, buf.ws, stream)
+        lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
+                           buf.winner, buf.tok_next, buf.conf_next, buf.arg_next, stream)
+    elif alpha is None:
         lopa_lmhead_conf(dims, buf.H, W, buf.rows, buf.row_ptr, buf.nb, buf.conf, buf.arg, None,
                          buf.ws, stream)
         lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
@@ -104,12 +114,15 @@ def decode_step(dims, k, tau, seed, Kp, Vp, W, buf: DecodeBuffers, stream=None,
 
 
 def decode_block(dims, k, tau, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, steps: int,
-                 log=None, stream=None, alpha=None, gamma=None) -> None:
+                 log=None, stream=None, alpha=None, gamma=None, temperature=None,
+                 sample_seed=0) -> None:
     """The initial pass and ``steps`` steps; ``log`` (device int32
-    [steps][B]) receives the tokens after each step."""
-    start_block(dims, seed, tok0, Kp, Vp, W, buf, stream)
+    [steps][B]) receives the tokens after each step.  With ``temperature``
+    pass s draws its tokens with seed sample_seed + s (0: the initial pass)."""
+    start_block(dims, seed, tok0, Kp, Vp, W, buf, stream, temperature, sample_seed)
     for s in range(steps):
-        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream, alpha, gamma)
+        decode_step(dims, k, tau, seed, Kp, Vp, W, buf, stream, alpha, gamma, temperature,
+                    sample_seed + s + 1)
         if log is not None:
             log[s].copy_(buf.tok)
 

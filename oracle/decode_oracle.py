@@ -206,7 +206,8 @@ def _explore_gaps(tok, conf, tau, k, gamma=None):
 
 
 def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = None,
-                 alpha: float | None = None, gamma: float | None = None) -> DecodeTrace:
+                 alpha: float | None = None, gamma: float | None = None,
+                 temperature: float | None = None, sample_seed: int = 0) -> DecodeTrace:
     """Decode inp.tok's masked positions: the initial pass, then verification
     steps (explore, verify, select and reuse) until none is masked.  The
     committed prefix Kp, Vp and the weight W come from ``inp``; every
@@ -220,6 +221,10 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
     H = round_like(branch_attn(st.Kp, st.Vp, st.Qb, st.Kb, st.Vb, 1, cfg.Hq, cfg.Hkv), st.Qb.dtype)
     masked = np.flatnonzero(tok == MASK)
     head = lmhead_conf(H[0, masked, :], inp.W)
+    if temperature is not None:   # pass s draws with seed sample_seed + s (0: the initial pass)
+        from .sample_oracle import lmhead_sample
+        smp = lmhead_sample(H[0, masked, :], inp.W, temperature, sample_seed, masked)
+        head = replace(head, conf=smp.conf, arg=smp.arg, margin=smp.margin)
     conf = np.zeros(cfg.B, np.float32)
     arg = np.full(cfg.B, -1, np.int32)
     conf[masked] = head.conf.astype(np.float32)
@@ -238,7 +243,8 @@ def decode_block(inp, seed: int, k: int, tau: float, max_steps: int | None = Non
         # explore with the state, then the projections of every branch's tokens
         br = branch_build(tok, conf, arg, k, np.float32(tau), cfg.nb_max, g32)
         st = block_inputs(inp, seed, br.br_tok.reshape(cfg.nb_max, cfg.B)[:br.nb])
-        out = verification_step(replace(st, tok=tok), conf, arg, k, tau, alpha, gamma)
+        out = verification_step(replace(st, tok=tok), conf, arg, k, tau, alpha, gamma,
+                                temperature, sample_seed + len(tr.steps) + 1)
         sel = out.sel
         bc = np.sort(np.asarray(sel.bconf[:out.br.nb], np.float64))[::-1]
         win_margin = float(bc[0] - bc[1]) if bc.size > 1 else np.inf

@@ -420,12 +420,16 @@ def initial_state(inp) -> tuple[np.ndarray, np.ndarray, HeadOut]:
 
 def verification_step(inp, conf, arg, k: int | None = None,
                       tau: float | None = None, alpha: float | None = None,
-                      gamma: float | None = None) -> StepOut:
+                      gamma: float | None = None, temperature: float | None = None,
+                      sample_seed: int = 0) -> StepOut:
     """One LoPA iteration: explore, verify (attention + LM head) and select.
 
     ``conf`` must be float32 (the library's input precision).  ``alpha``
     selects with ``branch_select_alpha`` instead of the mean confidence;
-    ``gamma`` is branch_build's confidence floor for lookahead candidates."""
+    ``gamma`` is branch_build's confidence floor for lookahead candidates;
+    ``temperature`` draws each row's token from softmax(l / T)
+    (sample_oracle.lmhead_sample, noise keyed by ``sample_seed``) instead of
+    the argmax, its confidence being the drawn token's probability."""
     cfg = inp.cfg
     k = cfg.k if k is None else k
     tau = cfg.tau if tau is None else tau
@@ -436,6 +440,10 @@ def verification_step(inp, conf, arg, k: int | None = None,
     Hrows = np.stack([H[r // cfg.B, r % cfg.B] for r in br.rows]) if len(br.rows) \
         else np.zeros((0, cfg.hidden))
     head = lmhead_conf(Hrows, inp.W)
+    if temperature is not None:
+        from .sample_oracle import lmhead_sample
+        smp = lmhead_sample(Hrows, inp.W, temperature, sample_seed, np.asarray(br.rows) % cfg.B)
+        head = HeadOut(smp.conf, smp.arg, smp.margin, None, head.ent)
     n = cfg.nb_max * cfg.B
     conf_pos = np.zeros(n)
     arg_pos = np.full(n, -1, dtype=np.int64)

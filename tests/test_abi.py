@@ -83,6 +83,10 @@ def test_null_pointers_and_k_rejected():
     assert L.lopa_branch_build_floor(ctypes.byref(d), 5, 0.9, 0.1, *([fake] * 8), None) == -1
     assert L.lopa_branch_build_floor(ctypes.byref(d), 0, 0.9, 0.1, None, *([fake] * 7),
                                      None) == -1
+    # sampling: temperature > 0 and finite
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.lopa_lmhead_sample(ctypes.byref(d), T, 1, *([fake] * 9), 1 << 30, None) == -1
+    assert L.lopa_lmhead_sample(ctypes.byref(d), 0.8, 1, None, *([fake] * 8), 1 << 30, None) == -1
     # entropy variant: ent is required
     assert L.lopa_lmhead_conf_ent(ctypes.byref(d), *([fake] * 7), None, None, fake, 1 << 30,
                                   None) == -1
@@ -108,8 +112,8 @@ def test_workspace_size_and_shortfall():
     split = _dims(L=4096, B=64, k_max=8)
     assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 64 * 7) * 130 * 4
     # the LM head alone needs rows x 256 vocabulary parts x (max, sum, argmax,
-    # entropy term)
-    head_need = 5 * 32 * 256 * 16
+    # entropy term or perturbed score, sampled logit)
+    head_need = 5 * 32 * 256 * 20
     fake = ctypes.c_void_p(16)
     L = lopa.lib()
     args = [fake] * 8
@@ -118,4 +122,4 @@ def test_workspace_size_and_shortfall():
     assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
                               need - 1, None) == -3
     f32 = _dims(dtype=lopa.F32, V=1000)
-    assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 16
+    assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 20

@@ -1,0 +1,118 @@
+"""GPU parity of temperature sampling in the LM head (lopa_lmhead_sample)
+against oracle/sample_oracle.py, and of blocks decoded with it.
+
+* Identical inputs (the oracle's rounded H): the drawn token where the
+  oracle's best-minus-second perturbed score exceeds 1e-3 (logits agree to
+  ~1e-5 relative, the noise to float32 rounding), the confidence (the drawn
+  token's probability at temperature T) within 1e-4 relative.
+* The GPU's draws follow softmax(l / T): token frequencies over many seeds
+  within four binomial standard deviations.
+* Blocks decoded with sampling, compared step by step while every decision
+  is clear-cut (as for greedy decoding; the margins are the perturbed ones).
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+import lookahead_decoding_amd as lopa
+import synth
+from lookahead_decoding_amd.decode import DecodeBuffers, decode_block
+from lookahead_decoding_amd.step import StepBuffers, dims_of, to_device
+from oracle import decode_oracle as D
+from oracle import lopa_oracle as O
+from oracle import sample_oracle as S
+from _parity import device_inputs
+
+pytestmark = pytest.mark.gpu
+M = O.MASK
+
+CASES = [
+    ("f32-tiny", dict(), 1.0),
+    ("bf16-mfma-ragged-V", dict(dtype="bf16", Hq=4, Hkv=2, d=64, V=1000, B=16, m=12, k=3), 0.7),
+    ("bf16-plain-hidden96", dict(dtype="bf16", Hq=3, Hkv=1, d=32, V=513, B=8, m=6, k=2), 1.1),
+    ("bf16-three-groups", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=2500, B=32, m=30, k=9), 0.8),
+    ("bf16-two-wide-groups", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=1900, B=64, m=50, k=8), 1.0),
+    ("bf16-7b-shape", dict(dtype="bf16", L=64, Hq=28, Hkv=4, d=128, V=152064, B=32, m=24, k=2),
+     0.9),
+]
+
+
+@pytest.mark.parametrize("name,ov,T", CASES, ids=[c[0] for c in CASES])
+def test_gpu_lmhead_sample(name, ov, T):
+    inp = synth.make_inputs(synth.TINY, **ov)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    nb = dims.nb_max
+    Hx = O.round_like(O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv),
+                      inp.Qb.dtype)
+    masked = np.flatnonzero(inp.tok == M)
+    r = np.array([b * cfg.B + p for b in range(nb) for p in masked], np.int32)
+    row_ptr = np.array([b * len(masked) for b in range(nb + 1)], np.int32)
+    rows = np.zeros(dims.nb_max * dims.B, np.int32)
+    rows[:len(r)] = r
+    Hin = O.f64_to_bf16(Hx) if cfg.dtype == "bf16" else Hx.astype(np.float32)
+    x = device_inputs(inp)
+    buf = StepBuffers(dims)
+    seed = 0xC0FFEE + len(name)
+    lopa.lopa_lmhead_sample(dims, T, seed, to_device(Hin), x["W"], to_device(rows),
+                            to_device(row_ptr), to_device(np.array([nb], np.int32)), buf.conf,
+                            buf.arg, None, buf.ws)
+    torch.cuda.synchronize()
+    ref = S.lmhead_sample(np.stack([Hx[q // cfg.B, q % cfg.B] for q in r]), inp.W, T, seed,
+                          r % cfg.B)
+    cg, ag = buf.conf.cpu().numpy()[r], buf.arg.cpu().numpy()[r]
+    sure = ref.margin > 1e-3
+    assert sure.mean() > 0.9
+    np.testing.assert_array_equal(ag[sure], ref.arg[sure])
+    np.testing.assert_allclose(cg[sure], ref.conf[sure], rtol=1e-4, atol=1e-7)
+
+
+def test_gpu_sample_frequencies():
+    """One row, six-entry vocabulary with chosen logits (H = the logits, W =
+    identity): 4000 seeds."""
+    V, T, n = 6, 0.8, 4000
+    l = np.array([1.0, 0.2, -0.5, 2.0, 0.0, 1.1], np.float32)
+    dims = lopa.Dims(L=0, B=1, Hq=1, Hkv=1, d=V, V=V, k_max=0, dtype=lopa.F32)
+    buf = StepBuffers(dims)
+    H = to_device(l.reshape(1, 1, V))
+    W = to_device(np.eye(V, dtype=np.float32))
+    rows, rp, one = (to_device(np.array([0], np.int32)), to_device(np.array([0, 1], np.int32)),
+                     to_device(np.array([1], np.int32)))
+    draws = torch.zeros(n, dtype=torch.int32, device="cuda")
+    for s in range(n):
+        lopa.lopa_lmhead_sample(dims, T, s, H, W, rows, rp, one, buf.conf, buf.arg, None, buf.ws)
+        draws[s] = buf.arg[0]
+    torch.cuda.synchronize()
+    counts = np.bincount(draws.cpu().numpy(), minlength=V)
+    p = softmax(l.astype(np.float64) / T)
+    assert np.all(np.abs(counts / n - p) <= 4 * np.sqrt(p * (1 - p) / n))
+
+
+SAMPLE_DECODE = [("T0.7-a", 0.7, 1000), ("T0.7-b", 0.7, 3000), ("T1.0", 1.0, 1000)]
+
+
+@pytest.mark.parametrize("name,T,ss", SAMPLE_DECODE, ids=[c[0] for c in SAMPLE_DECODE])
+def test_gpu_decode_block_sampled(name, T, ss):
+    ov = dict(dtype="bf16", L=100, B=32, m=20, Hq=8, Hkv=2, d=128, V=4096, k=3)
+    inp = synth.make_inputs(synth.TINY, **ov)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    k, tau, seed = 3, 0.9, 7
+    tr = D.decode_block(inp, seed, k, tau, temperature=T, sample_seed=ss)
+    m = int(np.sum(inp.tok == M))
+    buf = DecodeBuffers(dims)
+    x = {n: to_device(getattr(inp, n)) for n in ("Kp", "Vp", "W")}
+    log = torch.zeros(m, cfg.B, dtype=torch.int32, device="cuda")
+    decode_block(dims, k, tau, seed, inp.tok, x["Kp"], x["Vp"], x["W"], buf, m, log,
+                 temperature=T, sample_seed=ss)
+    torch.cuda.synchronize()
+    got = log.cpu().numpy()
+    compared = 0
+    for s, st in enumerate(tr.steps):
+        if not (st.fill_margin > 1e-2 and st.rank_gap > 1e-4 and st.tau_gap > 1e-4
+                and st.win_margin > 1e-3):
+            break
+        assert np.array_equal(got[s], st.tok), f"{name}: step {s}"
+        compared += 1
+    assert compared >= min(3, len(tr.steps))
