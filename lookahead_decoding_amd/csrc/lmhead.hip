@@ -333,7 +333,15 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     };
     for (int i = 0; i < total; ++i) {
       __syncthreads();
-      compute(i % kStages);
+      // in the last, partial pass a wave column whose vocabulary tiles all
+      // lie past the range only keeps step (its logits would all be dropped).
+      // Only the 4-column bodies have such columns (a 594-row range ends 82
+      // rows into a 256-row pass); the 2-column ones run unconditionally.
+      if constexpr (WX == 4) {
+        if (v_lo + (i / nch) * WROWS + wx * (32 * NVW) < v_hi) compute(i % kStages);
+      } else {
+        compute(i % kStages);
+      }
       if (i % nch == nch - 1) finish_pass(i / nch);
     }
   }
