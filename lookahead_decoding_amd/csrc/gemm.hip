@@ -18,6 +18,8 @@
 // v_mfma_f32_32x32x16_bf16 fragments from it.  The activation fragment is the
 // MFMA's A operand, so a lane's outputs run along one weight row and the
 // partial stores are 128-byte row segments.
+#include <type_traits>
+
 #include "gemm_plan.hpp"
 #include "stream_tile.hpp"
 
@@ -94,8 +96,9 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
-    auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NVW], u16x8 (&hf)[MTW])
-        __attribute__((always_inline)) {
+    auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NVW], u16x8 (&hf)[MTW],
+                     auto live) __attribute__((always_inline)) {
+      constexpr int LIVE = decltype(live)::value;
       const int s = j * 2 + lh;
 #pragma unroll
       for (int n = 0; n < NVW; ++n) {
@@ -103,20 +106,23 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
         wf[n] = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
       }
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
+      for (int mt = 0; mt < LIVE; ++mt) {
         const int r = (wy * MTW + mt) * 32 + ln;
         hf[mt] = *reinterpret_cast<const u16x8*>(base + (WROWS + r) * kRB + swz<kKC>(r, s) * 16);
       }
     };
-    auto compute = [&](int b) __attribute__((always_inline)) {
+    // LIVE = how many of the wave's activation tiles hold rows below M (the
+    // rest would only multiply padding)
+    auto compute = [&](int b, auto live) __attribute__((always_inline)) {
+      constexpr int LIVE = decltype(live)::value;
       const unsigned char* base = smem + b * BUF;
       u16x8 wf[2][NVW], hf[2][MTW];
-      frags(base, 0, wf[0], hf[0]);
+      frags(base, 0, wf[0], hf[0], live);
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        if (j + 1 < KS) frags(base, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
+        if (j + 1 < KS) frags(base, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1], live);
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
+        for (int mt = 0; mt < LIVE; ++mt)
 #pragma unroll
           for (int n = 0; n < NVW; ++n)
             acc[mt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -146,18 +152,26 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
           acc[mt][n] = f32x16{};
         }
     };
-    for (int i = 0; i < cnt; ++i) {
-      __syncthreads();
-      const int it = it0 + i;
-      const int u = it / v.nch;
-      const int kc = it - u * v.nch;
-      const int grp = u % v.groups;
-      // a wave whose activation tiles all lie past the last row only keeps step
-      if (grp * HROWS + wy * MTW * 32 < v.M) {
-        compute(i % kStages);
-        if (kc == v.nch - 1 || i == cnt - 1) flush(u);
+    auto run = [&](auto live) __attribute__((always_inline)) {
+      for (int i = 0; i < cnt; ++i) {
+        __syncthreads();
+        const int it = it0 + i;
+        const int u = it / v.nch;
+        const int kc = it - u * v.nch;
+        const int grp = u % v.groups;
+        // a wave whose activation tiles all lie past the last row only keeps step
+        if (grp * HROWS + wy * MTW * 32 < v.M) {
+          compute(i % kStages, live);
+          if (kc == v.nch - 1 || i == cnt - 1) flush(u);
+        }
       }
-    }
+    };
+    // with one row group, a wave whose later activation tiles hold only
+    // padding (160 rows in 256: tile 5) multiplies its first tile alone
+    if (MTW == 2 && v.groups == 1 && wy * 64 < v.M && wy * 64 + 32 >= v.M)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, MTW>{});
   }
 }
 
