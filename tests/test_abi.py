@@ -123,3 +123,66 @@ def test_workspace_size_and_shortfall():
                               need - 1, None) == -3
     f32 = _dims(dtype=lopa.F32, V=1000)
     assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 20
+
+
+def _model_dims(**kw):
+    base = dict(n_layers=2, inter=512, mask_id=999, rope_theta=1e6, rms_eps=1e-6)
+    base.update(kw)
+    return lopa.ModelDims(**base)
+
+
+def test_model_layout_and_workspace():
+    d = _dims(L=40, B=16, Hq=4, Hkv=2, d=64, V=1000, k_max=3)
+    md = _model_dims()
+    lay = lopa.model_layout(d, md)
+    h, qkv = 256, (4 + 4) * 64
+    # every tensor 256-byte aligned, in the documented order, sized as declared
+    assert lay.attn_norm == 0 and lay.wqkv == 512
+    assert lay.bqkv == lay.wqkv + qkv * h * 2
+    assert lay.wo == lay.bqkv + 1024 and lay.mlp_norm == lay.wo + h * h * 2
+    assert lay.wgu == lay.mlp_norm + 512 and lay.wd == lay.wgu + 2 * 512 * h * 2
+    assert lay.layer_stride == lay.wd + h * 512 * 2
+    assert lay.final_norm == 2 * lay.layer_stride
+    assert lay.embed == lay.final_norm + 512 and lay.lm_head == lay.embed + 1000 * h * 2
+    assert lay.total == lay.lm_head + 1000 * h * 2
+    assert lopa.model_workspace_bytes(d, md) > 0
+    # the 7B geometry: 15.2 GB of weights
+    d7 = _dims(L=512, B=32, Hq=28, Hkv=4, d=128, V=152064, k_max=4)
+    lay7 = lopa.model_layout(d7, _model_dims(n_layers=28, inter=18944, mask_id=151666))
+    assert lay7.total == 15231233024
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(md=dict(n_layers=0)), -1), (dict(md=dict(inter=0)), -1), (dict(md=dict(mask_id=1000)), -1),
+    (dict(md=dict(rope_theta=1.0)), -1), (dict(md=dict(rms_eps=-1.0)), -1),
+    (dict(d=dict(dtype=lopa.F32)), -2), (dict(md=dict(inter=100)), -2), (dict(d=dict(d=60)), -2),
+])
+def test_model_dims_rejected(bad, status):
+    dd = dict(L=40, B=16, Hq=4, Hkv=2, d=64, V=1000, k_max=3)
+    dd.update(bad.get("d", {}))
+    d = _dims(**dd)
+    md = _model_dims(**bad.get("md", {}))
+    out = lopa.ModelLayout()
+    assert lopa.lib().lopa_model_layout_of(ctypes.byref(d), ctypes.byref(md), ctypes.byref(out)) == status
+
+
+def test_model_calls_reject_null_and_small_workspace():
+    d = _dims(L=40, B=16, Hq=4, Hkv=2, d=64, V=1000, k_max=3)
+    md = _model_dims()
+    L = lopa.lib()
+    fake = ctypes.c_void_p(256)
+    need = lopa.model_workspace_bytes(d, md)
+    args = [fake, fake, fake, 40, fake, fake, fake, fake, fake]
+    assert L.lopa_branch_forward(ctypes.byref(d), ctypes.byref(md), *args, fake, need - 1,
+                                 None) == -3
+    a2 = list(args)
+    a2[4] = None                                   # br_tok
+    assert L.lopa_branch_forward(ctypes.byref(d), ctypes.byref(md), *a2, fake, need, None) == -1
+    a3 = list(args)
+    a3[3] = 39                                     # fewer cache rows than the prefix
+    assert L.lopa_branch_forward(ctypes.byref(d), ctypes.byref(md), *a3, fake, need, None) == -1
+    assert L.lopa_model_synth(ctypes.byref(d), ctypes.byref(md), 1, None, fake, fake, 40,
+                              None) == -1
+    # the commit must fit the cache
+    assert L.lopa_model_commit(ctypes.byref(d), ctypes.byref(md), fake, fake, fake, fake, fake,
+                               40, 30, None) == -1
