@@ -204,6 +204,23 @@ def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
         head_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         alg = model_bytes(dims, md)
         ach = alg["forward_bytes"] / (fwd_ms * 1e-3) / 1e9
+        # the block decoded with the model until nothing is masked
+        from lookahead_decoding_amd.model import ModelDecodeBuffers, model_decode_block
+        m = len(masked)
+        dbuf = ModelDecodeBuffers(dims, md)
+        log = torch.zeros(max(m, 1), B, dtype=torch.int32, device="cuda")
+        model_decode_block(model, dims, k, cfg.tau, tok, dbuf, m, log)
+        torch.cuda.synchronize()
+        got = log.cpu().numpy()
+        done = [s for s in range(m) if not np.any(got[s] == lopa.MASK)]
+        dsteps = done[0] + 1 if done else m
+        t0 = time.perf_counter()
+        for _ in range(2):
+            model_decode_block(model, dims, k, cfg.tau, tok, dbuf, dsteps)
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t0) / 2 * 1e3
+        decode = {"masked": m, "steps": dsteps, "tpf": round(m / dsteps, 3),
+                  "ms_per_block": round(dms, 2), "decoded_tokens_per_s": round(m / (dms * 1e-3), 1)}
         res = {"k": k, "branches": int(buf.nb.item()), "rows": nbm * B,
                "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 3),
                "forward_ms": round(fwd_ms, 3), "lmhead_ms": round(head_ms, 3),
@@ -211,8 +228,9 @@ def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(ach / HBM_PEAK_GBS, 4),
                                     "algorithmic_bytes": alg["forward_bytes"],
-                                    "mfma_tflops": round(alg["flops"] / (fwd_ms * 1e-3) / 1e12, 1)}}
-        del model, buf, fb
+                                    "mfma_tflops": round(alg["flops"] / (fwd_ms * 1e-3) / 1e12, 1)},
+               "decode": decode}
+        del model, buf, fb, dbuf
         torch.cuda.empty_cache()
         return res
 

@@ -356,8 +356,9 @@ int lopa_model_workspace_bytes(const lopa_dims* dims, const lopa_model_dims* md,
  * 9 lm_head, 10 prefix K, 11 prefix V (rows = prefix positions, columns =
  * Hkv*d).  Norm weights: 1 + ((x >> 27) - 16) / 128.  Other tensors:
  * ((x >> 8) - 2^23) * 2^(-24-s) rounded to bf16, with s = round(log2(sqrt(
- * fan_in / 12))) for the projections and the LM head, 2 for the biases, 1
- * for the embedding and -1 for the prefix keys and values.
+ * fan_in / 12))) for the projections, that minus 2 for the LM head (logits
+ * of spread ~4), 2 for the biases, 1 for the embedding and -1 for the prefix
+ * keys and values.
  * Out weights (lopa_model_layout_of().total bytes); Kp, Vp
  *     [n_layers][kv_layer_rows][Hkv][d]: rows 0..L-1 of every layer.
  */

@@ -352,7 +352,9 @@ extern "C" int lopa_model_synth(const lopa_dims* dims, const lopa_model_dims* md
   }
   gen(lay.final_norm, 1, s.hidden, 7, 0, kRuleNorm, 0);
   gen(lay.embed, dims->V, s.hidden, 8, 0, kRuleUniform, 1);
-  gen(lay.lm_head, dims->V, s.hidden, 9, 0, kRuleUniform, sh_hidden);
+  // the LM head four times wider than fan-in scaling: logits of spread ~4,
+  // like the trained model's, so confidences are not all near 1 / V
+  gen(lay.lm_head, dims->V, s.hidden, 9, 0, kRuleUniform, sh_hidden - 2);
   const int kvc = dims->Hkv * dims->d;
   const size_t kv_layer_bytes = kv_layer_rows * kvc * 2;
   for (int l = 0; l < md->n_layers && dims->L > 0; ++l) {

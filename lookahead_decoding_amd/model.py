@@ -12,6 +12,11 @@ from __future__ import annotations
 from . import (ModelDims, lopa_branch_build, lopa_branch_forward, lopa_branch_select,
                lopa_lmhead_conf, lopa_model_synth, model_layout, model_workspace_bytes)
 
+# A block decoded with the model repeats the step above from the initial
+# pass's state until no position is masked (model_decode_block), and
+# model_decode_sequence commits each decoded block's winner K/V of every
+# layer so the next block attends to it.
+
 # Qwen2.5-7B / Dream-7B geometry (hidden 3584 = 28 x 128)
 QWEN7B = dict(n_layers=28, inter=18944, mask_id=151666, rope_theta=1e6, rms_eps=1e-6)
 
@@ -82,3 +87,96 @@ def model_step(model: Model, k: int, tau: float, tok, conf, arg, buf, fb: Forwar
                      None, buf.ws, stream)
     lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg, buf.bconf,
                        buf.winner, buf.tok_next, buf.conf_next, buf.arg_next, stream)
+
+
+class ModelDecodeBuffers:
+    """State and per-step buffers of block decoding with the model."""
+
+    def __init__(self, dims, md: ModelDims, device="cuda"):
+        import torch
+        from .step import StepBuffers
+        self.step = StepBuffers(dims, device)
+        self.fwd = ForwardBuffers(dims, md, device)
+        B, nbm = dims.B, dims.nb_max
+        i32 = torch.int32
+        self.one = torch.ones(1, dtype=i32, device=device)
+        self.tok = torch.zeros(B, dtype=i32, device=device)
+        self.conf = torch.zeros(B, dtype=torch.float32, device=device)
+        self.arg = torch.zeros(B, dtype=i32, device=device)
+        self.tok0 = torch.zeros(nbm * B, dtype=i32, device=device)
+        self.rows0 = torch.zeros(nbm * B, dtype=i32, device=device)
+        self.row_ptr0 = torch.zeros(nbm + 1, dtype=i32, device=device)
+
+    def swap_state(self):
+        s = self.step
+        self.tok, s.tok_next = s.tok_next, self.tok
+        self.conf, s.conf_next = s.conf_next, self.conf
+        self.arg, s.arg_next = s.arg_next, self.arg
+
+
+def model_decode_block(model: Model, dims, k: int, tau: float, tok0, buf: ModelDecodeBuffers,
+                       steps: int, log=None, stream=None) -> None:
+    """Decode one block with the model: the initial pass (the block as it
+    stands in slot 0, the LM head on its masked positions), then ``steps``
+    verification steps, each build -> forward -> LM head -> select with the
+    winner's state swapped in.  ``dims`` carries the current prefix length
+    (dims.L rows of the model's cache are the committed prefix).  ``log``
+    (device int32 [steps][B]) receives the tokens after each step."""
+    import numpy as np
+    import torch
+    from . import MASK
+    tok0 = np.asarray(tok0, np.int32)
+    dev = buf.tok.device
+    B, nbm = dims.B, dims.nb_max
+    s = buf.step
+    buf.tok.copy_(torch.from_numpy(tok0).to(dev))
+    buf.tok0.copy_(torch.from_numpy(np.tile(tok0, nbm)).to(dev))
+    masked = np.flatnonzero(tok0 == MASK).astype(np.int32)
+    buf.rows0.zero_()
+    buf.rows0[:len(masked)] = torch.from_numpy(masked).to(dev)
+    buf.row_ptr0.fill_(len(masked))
+    buf.row_ptr0[0] = 0
+    forward(model, buf.tok0, buf.one, buf.fwd, stream, dims=dims)
+    s.conf.zero_()
+    s.arg.fill_(-1)
+    lopa_lmhead_conf(dims, buf.fwd.H, model.lm_head, buf.rows0, buf.row_ptr0, buf.one, s.conf,
+                     s.arg, None, s.ws, stream)
+    buf.conf.copy_(s.conf[:B])
+    buf.arg.copy_(s.arg[:B])
+    for i in range(steps):
+        lopa_branch_build(dims, k, tau, buf.tok, buf.conf, buf.arg, s.nb, s.br_tok, s.br_mask,
+                          s.rows, s.row_ptr, stream)
+        forward(model, s.br_tok, s.nb, buf.fwd, stream, dims=dims)
+        lopa_lmhead_conf(dims, buf.fwd.H, model.lm_head, s.rows, s.row_ptr, s.nb, s.conf, s.arg,
+                         None, s.ws, stream)
+        lopa_branch_select(dims, s.nb, s.br_mask, s.br_tok, s.conf, s.arg, s.bconf, s.winner,
+                           s.tok_next, s.conf_next, s.arg_next, stream)
+        buf.swap_state()
+        if log is not None:
+            log[i].copy_(buf.tok)
+
+
+def model_decode_sequence(model: Model, k: int, tau: float, blocks, buf: ModelDecodeBuffers,
+                          logs=None, stream=None) -> int:
+    """Decode ``blocks`` one after another with the model, committing each
+    decoded block's winner K/V of every layer (lopa_model_commit) at the end
+    of the prefix, so the next block attends to it.  The model's cache must
+    have room for the prefix plus len(blocks) * B rows.  Returns the final
+    prefix length."""
+    import numpy as np
+    from . import MASK, Dims, lopa_model_commit
+    import torch
+    d0 = model.dims
+    L = d0.L
+    zero = torch.zeros(1, dtype=torch.int32, device=buf.tok.device)
+    for j, tok0 in enumerate(blocks):
+        dj = Dims(L=L, B=d0.B, Hq=d0.Hq, Hkv=d0.Hkv, d=d0.d, V=d0.V, k_max=d0.k_max,
+                  dtype=d0.dtype)
+        m = int(np.sum(np.asarray(tok0) == MASK))
+        model_decode_block(model, dj, k, tau, tok0, buf, m, None if logs is None else logs[j],
+                           stream)
+        # with no step taken, slot 0 holds the block (written by the initial pass)
+        lopa_model_commit(dj, model.md, buf.step.winner if m else zero, buf.fwd.Kb, buf.fwd.Vb,
+                          model.Kp, model.Vp, model.kv_rows, L, stream)
+        L += d0.B
+    return L

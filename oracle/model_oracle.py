@@ -211,7 +211,8 @@ def synth_rows(seed: int, cfg: ModelCfg, tid: int, rows) -> np.ndarray:
     """Selected rows [len(rows)][hidden] of the embedding (tid 8) or the LM
     head (tid 9); the generator is counter-based, so a row can be drawn
     alone."""
-    shift = 1 if tid == TENSOR_ID["embed"] else fan_in_shift(cfg.hidden)
+    # the LM head is four times wider than fan-in scaling (logit spread ~4)
+    shift = 1 if tid == TENSOR_ID["embed"] else fan_in_shift(cfg.hidden) - 2
     quads = (cfg.hidden + 3) // 4
     key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], np.uint32)
     rows = np.asarray(rows, np.uint32)
@@ -316,3 +317,86 @@ def forward(seed: int, cfg: ModelCfg, L: int, br_tok: np.ndarray, layers=None,
         x, Kb[l], Vb[l] = layer_forward(cfg, layers[l], x, prefix[l][0], prefix[l][1], L,
                                         round_points)
     return ForwardOut(R(rmsnorm(x, final, cfg.rms_eps)), Kb, Vb)
+
+
+# ---------------------------------------------------------------------------
+# Decoding blocks with the model
+# ---------------------------------------------------------------------------
+
+def decode_block(seed: int, cfg: ModelCfg, L: int, tok0, k: int, tau: float, nb_max: int,
+                 layers=None, prefix=None, max_steps: int | None = None):
+    """Decode tok0's masked positions with the model: the initial pass (the
+    block alone through the model, the LM head on its masked positions),
+    then verification steps -- explore (lopa_oracle.branch_build), every
+    branch through the model, the LM head on the still-masked rows, select
+    and reuse -- until none is masked (news article, section "LoPA 的核心设计：
+    前瞻并行与分支验证"; the LM head weight is the model's).  Returns the trace
+    (decode_oracle.DecodeTrace) and the winner's block keys and values of
+    every layer from the last pass ([n_layers][B][Hkv][d] each), the cache a
+    commit appends."""
+    from .decode_oracle import DecodeStep, DecodeTrace, _explore_gaps
+    from .lopa_oracle import branch_build, branch_select, lmhead_conf
+    if layers is None:
+        layers = [synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
+    if prefix is None:
+        prefix = [synth_prefix(seed, cfg, l, L) for l in range(cfg.n_layers)]
+    W = synth_rows(seed, cfg, TENSOR_ID["lm_head"], np.arange(cfg.V)).astype(np.float32)
+    B = len(tok0)
+    tok = np.asarray(tok0, np.int32).copy()
+    out = forward(seed, cfg, L, tok[None], layers, prefix)
+    masked = np.flatnonzero(tok == MASK)
+    head = lmhead_conf(out.H[0, masked, :], W)
+    conf = np.zeros(B, np.float32)
+    arg = np.full(B, -1, np.int32)
+    conf[masked] = head.conf.astype(np.float32)
+    arg[masked] = head.arg
+    margin = np.full(B, np.inf)
+    margin[masked] = head.margin
+    tr = DecodeTrace(tok.copy(), conf.copy(), arg.copy(),
+                     float(head.margin.min()) if head.margin.size else np.inf)
+    Kw, Vw = out.Kb[:, 0], out.Vb[:, 0]
+    limit = int(masked.size) if max_steps is None else max_steps
+    for _ in range(limit):
+        if not np.any(tok == MASK):
+            break
+        rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k)
+        br = branch_build(tok, conf, arg, k, np.float32(tau), nb_max)
+        out = forward(seed, cfg, L, br.br_tok[:br.nb], layers, prefix)
+        rows = np.asarray(br.rows)
+        n = nb_max * B
+        conf_pos, arg_pos, margin_pos = np.zeros(n), np.full(n, -1), np.full(n, np.inf)
+        if rows.size:
+            h = lmhead_conf(np.stack([out.H[r // B, r % B] for r in rows]), W)
+            conf_pos[rows], arg_pos[rows], margin_pos[rows] = h.conf, h.arg, h.margin
+        sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
+        bc = np.sort(np.asarray(sel.bconf[:br.nb], np.float64))[::-1]
+        new_tok = np.asarray(sel.tok_next, np.int32)
+        filled = (tok == MASK) & (new_tok != MASK)
+        tr.steps.append(DecodeStep(br.nb, int(sel.winner), new_tok.copy(), int(filled.sum()),
+                                   float(margin[filled].min()) if filled.any() else np.inf,
+                                   rank_gap, tau_gap,
+                                   float(bc[0] - bc[1]) if bc.size > 1 else np.inf))
+        w = int(sel.winner)
+        margin = np.where(new_tok == MASK, margin_pos[w * B:(w + 1) * B], np.inf)
+        tok = new_tok
+        conf = np.asarray(sel.conf_next, np.float32)
+        arg = np.asarray(sel.arg_next, np.int32)
+        Kw, Vw = out.Kb[:, w], out.Vb[:, w]
+    return tr, Kw, Vw
+
+
+def decode_sequence(seed: int, cfg: ModelCfg, L: int, blocks, k: int, tau: float, nb_max: int):
+    """Decode ``blocks`` one after another, appending each decoded block's
+    winner keys and values of every layer to that layer's prefix (the
+    commit of the news article's section "系统级创新：LoPA-Dist 分布式推理",
+    one GPU).  Returns the traces and the final per-layer prefixes."""
+    layers = [synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
+    prefix = [synth_prefix(seed, cfg, l, L) for l in range(cfg.n_layers)]
+    traces = []
+    for tok0 in blocks:
+        tr, Kw, Vw = decode_block(seed, cfg, L, tok0, k, tau, nb_max, layers, prefix)
+        traces.append(tr)
+        prefix = [(np.concatenate([prefix[l][0], Kw[l]]), np.concatenate([prefix[l][1], Vw[l]]))
+                  for l in range(cfg.n_layers)]
+        L += len(tok0)
+    return traces, prefix
