@@ -46,8 +46,9 @@ class Model:
     def tensor(self, offset: int, *shape):
         """bf16 view of the weight buffer at a byte offset."""
         import math
+        import torch
         n = math.prod(shape) * 2
-        return self.weights[offset:offset + n].view(__import__("torch").bfloat16).view(*shape)
+        return self.weights[offset:offset + n].view(torch.bfloat16).view(*shape)
 
     @property
     def lm_head(self):
