@@ -12,6 +12,9 @@
 //
 // Kernels write per-(row, vocabulary part) online-softmax partials
 // (max, sum exp(l - max), argmax); a merge kernel folds the parts of a row.
+// Two more modes ride the same pass: the entropy term sum exp(l - max)(l - max)
+// (lopa_lmhead_conf_ent) and temperature sampling by Gumbel-max
+// (lopa_lmhead_sample: partials over l / T plus the best perturbed score).
 //   k_lmhead_mfma   bf16.  One persistent workgroup per compute unit owns a
 //                   balanced contiguous vocabulary range and every LM-head
 //                   row of its row group.  Four producer waves move 64-wide
