@@ -48,6 +48,29 @@ def test_gpu_build_floor_bit_exact(seed):
     assert_build_equal(g, O.branch_build(tok, conf, arg, k, tau, nbm, gamma))
 
 
+def test_gpu_build_floor_edges():
+    """One position; nothing masked; everything masked with the floor
+    exactly at every confidence (ties at the floor are candidates)."""
+    for tok, conf, k, gamma in (
+            (np.array([M], np.int32), np.array([0.2], np.float32), 0, 0.5),
+            (np.array([3, 4, 5], np.int32), np.zeros(3, np.float32), 2, 0.1),
+            (np.full(8, M, np.int32), np.full(8, 0.25, np.float32), 3, 0.25)):
+        B = len(tok)
+        arg = np.arange(B, dtype=np.int32) + 10
+        dims = lopa.Dims(L=0, B=B, Hq=1, Hkv=1, d=8, V=100, k_max=3, dtype=lopa.F32)
+        buf = StepBuffers(dims)
+        lopa.lopa_branch_build_floor(dims, k, np.float32(0.9), np.float32(gamma), to_device(tok),
+                                     to_device(conf), to_device(arg), buf.nb, buf.br_tok,
+                                     buf.br_mask, buf.rows, buf.row_ptr)
+        torch.cuda.synchronize()
+        nbm = dims.nb_max
+        g = dict(nb=int(buf.nb.item()), br_tok=buf.br_tok.cpu().numpy().reshape(nbm, B),
+                 br_mask=buf.br_mask.cpu().numpy().reshape(nbm, B), rows=buf.rows.cpu().numpy(),
+                 row_ptr=buf.row_ptr.cpu().numpy())
+        assert_build_equal(g, O.branch_build(tok, conf, arg, k, np.float32(0.9), nbm,
+                                             np.float32(gamma)))
+
+
 FLOOR_DECODE = [
     ("floor-0.25", 0.25, 7), ("floor-0.3", 0.3, 21), ("floor-0.4", 0.4, 24),
 ]

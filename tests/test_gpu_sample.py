@@ -35,6 +35,8 @@ CASES = [
     ("bf16-two-wide-groups", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=1900, B=64, m=50, k=8), 1.0),
     ("bf16-7b-shape", dict(dtype="bf16", L=64, Hq=28, Hkv=4, d=128, V=152064, B=32, m=24, k=2),
      0.9),
+    # one vocabulary entry: always token 0 with probability 1
+    ("bf16-mfma-V1", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=1, B=4, m=4, k=1), 0.8),
 ]
 
 
