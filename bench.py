@@ -256,7 +256,14 @@ def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds or n >= 50:
             break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n} full oracle step(s) of the same workload (build, per-branch fp64 "
                       f"attention, fp64 LM head over all {inp.cfg.V} entries of every listed row, "
                       f"select) in {el:.1f} s; cores = BLAS threads of the fp64 matmul"}
@@ -328,14 +335,31 @@ def main():
     for _ in range(args.warmup):
         graph.replay() if graph else step()
     torch.cuda.synchronize()
+    # an event at every step boundary, for the distribution of step times
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    step_ev[0].record(stream)
     for i in range(args.steps):
         graph.replay() if graph else timed_step(i)
+        step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
     head_timed_us = None if graph else \
         float(np.mean([a.elapsed_time(b) for a, b in head_ev])) * 1e3
+    step_us = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]) * 1e3
+
+    # the same step with no lookahead branch (k = 0: the anchor alone), for the
+    # cost of the extra branches
+    k0_us = None
+    if cfg.k > 0 and not graph:
+        for i in range(args.warmup + 50):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+            run_step(dims, 0, cfg.tau, x, buf)
+        torch.cuda.synchronize()
+        k0_us = (time.perf_counter() - t1) / 50 * 1e6
 
     # Per-call durations with HIP events on the stream the calls run on.
     K = max(20, min(args.steps, 100))
@@ -406,6 +430,13 @@ def main():
         "step_hbm_frac": round(alg["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round((alg["head_flops"] + alg["attn_flops"]) / (ms * 1e-3) / 1e12
                                 / BF16_PEAK_TFLOPS, 4),
+        # max(time at the HBM roof, time at the MFMA roof) / measured step time
+        "step_roofline_frac": round(max(alg["step_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                        (alg["head_flops"] + alg["attn_flops"]) /
+                                        (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
+        "step_us_k0": None if k0_us is None else round(k0_us, 2),
+        "t_k_over_t_k0": None if k0_us is None else round(ms * 1e3 / k0_us, 4),
         "call_us": {"branch_build": round(float(call_us[0]), 2),
                     "branch_attn": round(float(call_us[1]), 2),
                     "lmhead_conf": round(float(call_us[2]), 2),
