@@ -25,15 +25,18 @@
 
 namespace lopa {
 
-constexpr int kGemmStage = (256 + 128) * kRB;   // largest BUF of the bodies
-constexpr int kGemmSmem = kStages * kGemmStage;
+constexpr int kGemmSmem = 3 * (256 + 160) * kRB;   // largest S x stage of the bodies
 
-template <int WX, int NVW, int MTW>
+// S LDS stages of HS activation rows (HS <= HROWS: a body that stages fewer
+// rows than its waves cover serves one row group of at most HS rows).
+template <int WX, int NVW, int MTW, int S, int HS>
 __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned short* __restrict__ X,
                                           const unsigned short* __restrict__ W,
                                           float* __restrict__ P, unsigned char* smem) {
   using T = StreamTile<WX, NVW, MTW>;
-  constexpr int WROWS = T::WROWS, HROWS = T::HROWS, BUF = T::BUF, WP = T::WP, HP = T::HP;
+  constexpr int WROWS = T::WROWS, HROWS = T::HROWS, WP = T::WP;
+  constexpr int BUF = (WROWS + HS) * kRB, HP = HS / 32;
+  static_assert(HS % 32 == 0 && HS <= HROWS && S >= 3 && S * BUF <= kGemmSmem, "body shape");
   constexpr int KS = kKC / 16;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -55,7 +58,7 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
         const_cast<unsigned short*>(X), 0, v.M * row_bytes, 0x00020000);
     const int wv = (8 * pw + r8) * row_bytes + ls * 16;
     auto issue = [&](int j) __attribute__((always_inline)) {
-      unsigned char* dst = smem + (j % kStages) * BUF;
+      unsigned char* dst = smem + (j % S) * BUF;
       j = min(j, cnt - 1);
       const int it = it0 + j;
       const int u = it / v.nch;
@@ -76,12 +79,12 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
       }
     };
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) issue(u);
-    wait_vmcnt<(kStages - 2) * (WP + HP)>();
+    for (int u = 0; u < S - 1; ++u) issue(u);
+    wait_vmcnt<(S - 2) * (WP + HP)>();
     __builtin_amdgcn_s_barrier();
     for (int i = 0; i + 1 < cnt; ++i) {
-      issue(i + kStages - 1);
-      wait_vmcnt<(kStages - 2) * (WP + HP)>();
+      issue(i + S - 1);
+      wait_vmcnt<(S - 2) * (WP + HP)>();
       __builtin_amdgcn_s_barrier();
     }
     wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
@@ -132,21 +135,26 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
     };
     // acc[mt][n][q] = Y[row (wy*MTW + mt)*32 + 8(q/4) + 4lh + q%4 of the group]
     //                  [col (wx*NVW + n)*32 + ln of the weight block]
-    auto flush = [&](int u) {
+    auto flush = [&](int u, auto live) __attribute__((always_inline)) {
+      constexpr int LIVE = decltype(live)::value;
       const int wb = u / v.groups;
       const int grp = u - wb * v.groups;
       const int slot = g - v.first_wg(u);
       const int mg = min(v.M - grp * HROWS, HROWS);
       const int ng = min(v.N - wb * WROWS, WROWS);
       float* tile = P + v.at(u, slot, 0, 0);
+      // the lane's first row, opaque to the compiler so the 16 x MTW x NVW
+      // store addresses are formed here and not kept live across the K loop
+      int r0 = wy * MTW * 32 + 4 * lh;
+      __asm__ volatile("" : "+v"(r0));
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
+      for (int mt = 0; mt < LIVE; ++mt)
 #pragma unroll
         for (int n = 0; n < NVW; ++n) {
           const int c = (wx * NVW + n) * 32 + ln;
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const int r = (wy * MTW + mt) * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
+            const int r = r0 + mt * 32 + 8 * (q >> 2) + (q & 3);
             if (r < mg && c < ng) tile[r * WROWS + c] = acc[mt][n][q];
           }
           acc[mt][n] = f32x16{};
@@ -161,26 +169,36 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
         const int grp = u % v.groups;
         // a wave whose activation tiles all lie past the last row only keeps step
         if (grp * HROWS + wy * MTW * 32 < v.M) {
-          compute(i % kStages, live);
-          if (kc == v.nch - 1 || i == cnt - 1) flush(u);
+          compute(i % S, live);
+          if (kc == v.nch - 1 || i == cnt - 1) flush(u, live);
         }
       }
     };
     // with one row group, a wave whose later activation tiles hold only
-    // padding (160 rows in 256: tile 5) multiplies its first tile alone
-    if (MTW == 2 && v.groups == 1 && wy * 64 < v.M && wy * 64 + 32 >= v.M)
-      run(std::integral_constant<int, 1>{});
-    else
+    // padding (160 rows in 256: tile 5) skips them: two-tile waves multiply
+    // their live tile alone, three-tile waves (rows 0..95 or 96..191, 160
+    // staged) their first two, which always lie within the staged rows
+    const int live = v.groups == 1 ? (v.M - wy * MTW * 32 + 31) >> 5 : MTW;
+    if constexpr (MTW == 5) {
+      run(std::integral_constant<int, 5>{});   // one group of more than 128 rows
+    } else if constexpr (MTW == 3) {
+      if (live <= 2) run(std::integral_constant<int, 2>{});
+      else run(std::integral_constant<int, 3>{});
+    } else if constexpr (MTW == 2) {
+      if (live == 1) run(std::integral_constant<int, 1>{});
+      else run(std::integral_constant<int, 2>{});
+    } else {
       run(std::integral_constant<int, MTW>{});
+    }
   }
 }
 
-template <int WX, int NVW, int MTW>
+template <int WX, int NVW, int MTW, int S, int HS>
 __global__ void __launch_bounds__(kStreamThreads)
 k_gemm_stream(GemmView v, const unsigned short* __restrict__ X,
               const unsigned short* __restrict__ W, float* __restrict__ P) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kGemmSmem];
-  gemm_body<WX, NVW, MTW>(v, X, W, P, smem);
+  gemm_body<WX, NVW, MTW, S, HS>(v, X, W, P, smem);
 }
 
 // Enqueue Y = X W^T as partial tiles into P (v.partial_bytes() bytes).
@@ -188,9 +206,21 @@ int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short
                 hipStream_t stream) {
   const dim3 grid(v.G), block(kStreamThreads);
   switch (v.body) {
-    case 0: hipLaunchKernelGGL((k_gemm_stream<4, 2, 1>), grid, block, 0, stream, v, X, W, P); break;
-    case 1: hipLaunchKernelGGL((k_gemm_stream<4, 2, 2>), grid, block, 0, stream, v, X, W, P); break;
-    default: hipLaunchKernelGGL((k_gemm_stream<2, 2, 2>), grid, block, 0, stream, v, X, W, P); break;
+    case 0:
+      hipLaunchKernelGGL((k_gemm_stream<4, 2, 1, 3, 64>), grid, block, 0, stream, v, X, W, P);
+      break;
+    case 1:
+      hipLaunchKernelGGL((k_gemm_stream<4, 2, 2, 3, 128>), grid, block, 0, stream, v, X, W, P);
+      break;
+    case 3:
+      hipLaunchKernelGGL((k_gemm_stream<4, 1, 3, 4, 160>), grid, block, 0, stream, v, X, W, P);
+      break;
+    case 4:
+      hipLaunchKernelGGL((k_gemm_stream<8, 1, 5, 3, 160>), grid, block, 0, stream, v, X, W, P);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_stream<2, 2, 2, 3, 256>), grid, block, 0, stream, v, X, W, P);
+      break;
   }
   return hipGetLastError() == hipSuccess ? LOPA_OK : LOPA_ERR_HIP;
 }

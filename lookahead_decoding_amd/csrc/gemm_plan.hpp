@@ -22,7 +22,9 @@ constexpr int kSlotTableMax = 4096;       // units whose slot counts a consumer 
 // unit is written exactly once.
 struct GemmView {
   int M, N, K;
-  // activation rows x weight rows per pass: 0: 64 x 256; 1: 128 x 256; 2: 256 x 128
+  // activation rows (staged per K chunk) x weight rows per pass, LDS stages:
+  // 0: 64 x 256, 3; 1: 128 x 256, 3; 2: 256 x 128, 3; 3: 160 x 128, 4;
+  // 4: 160 x 256, 3.  Bodies 3 and 4 stage only the 160 rows they serve.
   int body;
   int hrows, wrows;
   int hshift, wshift;   // log2 of hrows, wrows
@@ -55,7 +57,9 @@ struct GemmView {
       tab[u] = static_cast<unsigned char>(last_wg(u) - first_wg(u) + 1);
   }
   // Y[row][col .. col+3] (col % 4 == 0; the four columns share a unit); the
-  // slot loads are issued four at a time before any is added.
+  // slot loads are issued BATCH at a time before any is added, and the slots
+  // are added in slot order whatever BATCH is.
+  template <int BATCH = 4>
   __device__ float4 sum4(const float* __restrict__ P, const unsigned char* tab, int row,
                          int col) const {
     const int grp = row >> hshift, wb = col >> wshift;
@@ -65,13 +69,13 @@ struct GemmView {
         P + at(u, 0, row - (grp << hshift), col - (wb << wshift)));
     const size_t stride = tile_elems() / 4;
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < ns; s0 += 4) {
-      float4 t[4];
+    for (int s0 = 0; s0 < ns; s0 += BATCH) {
+      float4 t[BATCH];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < BATCH; ++j)
         t[j] = s0 + j < ns ? p[(s0 + j) * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < BATCH; ++j) {
         y.x += t[j].x;
         y.y += t[j].y;
         y.z += t[j].z;
@@ -88,10 +92,21 @@ inline GemmView gemm_view(int M, int N, int K, int max_wgs = kGemmMaxWorkgroups)
   v.M = M;
   v.N = N;
   v.K = K;
+  // hrows is the partial tile's row count (a power of two); bodies 3 and 4
+  // hold a single row group (M <= the 160 rows they stage).  Above 128 rows a
+  // wide weight (more than 64 blocks of 256 rows) takes the 256-row weight
+  // tile; a narrow one keeps 128 rows, as wider blocks would split its K
+  // range further and multiply the partial tiles.
   if (M <= 64) {
     v.body = 0; v.hrows = 64; v.wrows = 256;
   } else if (M <= 128) {
     v.body = 1; v.hrows = 128; v.wrows = 256;
+  } else if (M <= 160) {
+    if (N > 64 * 256) {
+      v.body = 4; v.hrows = 256; v.wrows = 256;
+    } else {
+      v.body = 3; v.hrows = 256; v.wrows = 128;
+    }
   } else {
     v.body = 2; v.hrows = 256; v.wrows = 128;
   }

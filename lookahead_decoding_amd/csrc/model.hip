@@ -64,14 +64,20 @@ k_synth_tensor(unsigned short* __restrict__ out, int rows, int cols, unsigned id
 }
 
 // ---------------------------------------------------------------------------
-// Row-wise kernels (one workgroup of 256 threads per activation row)
+// Row-wise kernels (one workgroup of kRowThreads threads per activation row:
+// at hidden <= 4 * kRowThreads every thread owns one group of four columns,
+// so a row's loads are all issued at once)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
+constexpr int kRowThreads = 1024;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float s = red[0] + red[1] + red[2] + red[3];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowThreads / 64; ++i) s += red[i];
   __syncthreads();
   return s;
 }
@@ -82,9 +88,9 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 __device__ __forceinline__ void norm_row(const float* __restrict__ xr, float ss, int hidden,
                                          float eps, const unsigned short* __restrict__ g,
                                          unsigned short* __restrict__ hr, float* red) {
-  const float tot = block_sum_256(ss, red);
+  const float tot = block_sum(ss, red);
   const float rs = 1.f / sqrtf(tot / static_cast<float>(hidden) + eps);
-  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+  for (int n = 4 * threadIdx.x; n < hidden; n += 4 * kRowThreads) {
     const float4 x = *reinterpret_cast<const float4*>(xr + n);
     const ushort4 gg = *reinterpret_cast<const ushort4*>(g + n);
     ushort4 o;
@@ -98,18 +104,18 @@ __device__ __forceinline__ void norm_row(const float* __restrict__ xr, float ss,
 
 // Embedding of each row's token (the mask token's row where masked) into the
 // residual stream, then the first layer's input norm.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRowThreads)
 k_embed_norm(int hidden, int V, int mask_id, float eps, const int32_t* __restrict__ tok,
              const unsigned short* __restrict__ E, const unsigned short* __restrict__ g,
              float* __restrict__ x, unsigned short* __restrict__ h) {
-  __shared__ float red[4];
+  __shared__ float red[kRowThreads / 64];
   const int r = blockIdx.x;
   const int t = tok[r];
   const int e = t == LOPA_MASK_TOKEN ? mask_id : min(max(t, 0), V - 1);
   float* xr = x + static_cast<size_t>(r) * hidden;
   const unsigned short* er = E + static_cast<size_t>(e) * hidden;
   float ss = 0.f;
-  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+  for (int n = 4 * threadIdx.x; n < hidden; n += 4 * kRowThreads) {
     const ushort4 ev = *reinterpret_cast<const ushort4*>(er + n);
     const float4 v = make_float4(bf16_bits_to_f32(ev.x), bf16_bits_to_f32(ev.y),
                                  bf16_bits_to_f32(ev.z), bf16_bits_to_f32(ev.w));
@@ -124,11 +130,11 @@ k_embed_norm(int hidden, int V, int mask_id, float eps, const int32_t* __restric
 
 // x[r] += (the projection's row r, summed from its partial tiles), then the
 // next norm of the row.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRowThreads)
 k_residual_norm(GemmView v, const float* __restrict__ P, float eps,
                 const unsigned short* __restrict__ g, float* __restrict__ x,
                 unsigned short* __restrict__ h) {
-  __shared__ float red[4];
+  __shared__ float red[kRowThreads / 64];
   __shared__ unsigned char tab[kSlotTableMax];
   v.load_slots(tab);
   __syncthreads();
@@ -136,9 +142,9 @@ k_residual_norm(GemmView v, const float* __restrict__ P, float eps,
   const int hidden = v.N;
   float* xr = x + static_cast<size_t>(r) * hidden;
   float ss = 0.f;
-  for (int n = 4 * threadIdx.x; n < hidden; n += 1024) {
+  for (int n = 4 * threadIdx.x; n < hidden; n += 4 * kRowThreads) {
     float4 y = *reinterpret_cast<const float4*>(xr + n);
-    const float4 d = v.sum4(P, tab, r, n);
+    const float4 d = v.sum4<8>(P, tab, r, n);
     y.x += d.x;
     y.y += d.y;
     y.z += d.z;
@@ -417,7 +423,7 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
   const int nrope = dims->B * (dims->d / 2);
   hipLaunchKernelGGL(k_rope_table, dim3((nrope + 255) / 256), dim3(256), 0, stream, dims->B,
                      dims->L, dims->d, log2_theta, rope);
-  hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(256), 0, stream, s.hidden, dims->V, md->mask_id,
+  hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(kRowThreads), 0, stream, s.hidden, dims->V, md->mask_id,
                      md->rms_eps, br_tok, wt(lay.embed), wt(lay.layer0 + lay.attn_norm), x, h);
   LOPA_LAUNCH_CHECK();
   for (int l = 0; l < md->n_layers; ++l) {
@@ -438,7 +444,7 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
                                aws_bytes, stream)) != LOPA_OK)
       return st;
     if ((st = gemm_launch(gm.o, ho, wt(lb + lay.wo), P, stream)) != LOPA_OK) return st;
-    hipLaunchKernelGGL(k_residual_norm, dim3(M), dim3(256), 0, stream, gm.o, P, md->rms_eps,
+    hipLaunchKernelGGL(k_residual_norm, dim3(M), dim3(kRowThreads), 0, stream, gm.o, P, md->rms_eps,
                        wt(lb + lay.mlp_norm), x, h);
     LOPA_LAUNCH_CHECK();
     // MLP block
@@ -451,7 +457,7 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
     const bool last = l + 1 == md->n_layers;
     const unsigned short* gnext =
         last ? wt(lay.final_norm) : wt(lb + lay.layer_stride + lay.attn_norm);
-    hipLaunchKernelGGL(k_residual_norm, dim3(M), dim3(256), 0, stream, gm.down, P, md->rms_eps,
+    hipLaunchKernelGGL(k_residual_norm, dim3(M), dim3(kRowThreads), 0, stream, gm.down, P, md->rms_eps,
                        gnext, x, last ? static_cast<unsigned short*>(H) : h);
     LOPA_LAUNCH_CHECK();
   }
