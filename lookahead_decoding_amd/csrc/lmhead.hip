@@ -262,8 +262,11 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
   } else {
     // ---------------- compute waves ----------------
-    const int wx = w % WX;
-    const int wy = w / WX;
+    // wave -> (vocabulary column, row group).  Wave w runs on SIMD w mod 4;
+    // with four columns SIMD s holds columns s/2 and s/2 + 2, so the live
+    // columns of a partial last pass are spread over all four SIMDs.
+    const int wx = WX == 4 ? w >> 1 : w % WX;
+    const int wy = WX == 4 ? w & 1 : w / WX;
     const int ln = lane & 31;     // MFMA row / column within a 32-tile
     const int lh = lane >> 5;     // which 8 of the 16 K values of a step
     f32x16 acc[MTW][NVW];
