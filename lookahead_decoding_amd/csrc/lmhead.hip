@@ -154,6 +154,7 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
 constexpr int kRunRows = 512;    // running partials: compute-wave columns x rows
 constexpr int kHeadThreads = kStreamThreads;
 constexpr int kHeadStage = (256 + 128) * kRB;        // largest BUF of the bodies below
+constexpr int kTailStages = 4;   // stages of a short last pass (half-width weight rows)
 constexpr int kHeadSmem = kStages * kHeadStage + kRunRows * static_cast<int>(sizeof(SPartial));
 
 // One persistent workgroup owns a contiguous, balanced vocabulary range
@@ -204,8 +205,19 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   const int v_hi = min(static_cast<int>(static_cast<long long>(part + 1) * t16 / nparts) * 16, V);
   const int npass = (v_hi - v_lo + WROWS - 1) / WROWS;
   const int nch = hidden / kKC;
-  const int total = npass * nch;
   const int rot = ((part >> 3) * nch / 32) % nch;
+  // A last pass of at most WROWS / 2 vocabulary rows (82 of 256 at V = 152064
+  // over 256 parts) runs as a second pipeline (the tail) whose kTailStages
+  // stages hold only WROWS / 2 weight rows: with its few rows a chunk is
+  // latency-bound, and the smaller stages keep one more chunk in flight.
+  // Only the four-column layout has such a tail; its upper two columns idle.
+  constexpr bool HAS_TAIL = WX == 4;
+  constexpr int TROWS = WROWS / 2, TBUF = (TROWS + T::HROWS) * kRB, TWP = WP / 2;
+  static_assert(!HAS_TAIL || kTailStages * TBUF <= kStages * BUF, "tail stages");
+  const int rem = v_hi - v_lo - (npass - 1) * WROWS;   // rows of the last pass
+  const bool tail = HAS_TAIL && npass > 0 && rem <= TROWS;
+  const int total_a = (tail ? npass - 1 : npass) * nch;   // chunks of the full-width pipeline
+  const int total_b = tail ? nch : 0;                     // chunks of the tail
 
   RP* run = reinterpret_cast<RP*>(smem + kStages * kHeadStage);
   for (int r = tid; r < kRunRows; r += kHeadThreads) {
@@ -230,33 +242,50 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
 #pragma unroll
     for (int p = 0; p < HP; ++p)
       hv[p] = rows[row0 + min(8 * (4 * p + pw) + r8, Mg - 1)] * row_bytes + ls * 16;
-    // chunk i -> stage i % kStages; past the end the last chunk is loaded
-    // again into the free stage so every iteration issues the same count
-    auto issue = [&](int i) __attribute__((always_inline)) {
-      unsigned char* dst = smem + (i % kStages) * BUF;
-      i = min(i, total - 1);
-      const int pass = i / nch;
-      int kc = i - pass * nch + rot;
-      kc = kc >= nch ? kc - nch : kc;
-      const int sw = pass * WROWS * row_bytes + kc * kRB;
+    // One pipeline over chunks c0 .. c0 + cnt - 1: chunk c0 + i -> stage i % S
+    // of BUFX bytes (WPX * 32 weight rows, then the activation rows); past the
+    // end the last chunk is loaded again into the free stage so every
+    // iteration issues the same count.  One barrier per chunk.
+    auto pipeline = [&](auto s_c, auto wp_c, int c0, int cnt) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value, WPX = decltype(wp_c)::value;
+      constexpr int BUFX = (WPX * 32 + T::HROWS) * kRB;
+      auto issue = [&](int i) __attribute__((always_inline)) {
+        unsigned char* dst = smem + (i % S) * BUFX;
+        const int c = c0 + min(i, cnt - 1);
+        const int pass = c / nch;
+        int kc = c - pass * nch + rot;
+        kc = kc >= nch ? kc - nch : kc;
+        const int sw = pass * WROWS * row_bytes + kc * kRB;
 #pragma unroll
-      for (int p = 0; p < WP; ++p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + pw) * 1024), 16, wv,
-                                                 sw + 32 * p * row_bytes, 0, kWeightAux);
+        for (int p = 0; p < WPX; ++p)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + pw) * 1024), 16, wv,
+                                                   sw + 32 * p * row_bytes, 0, kWeightAux);
 #pragma unroll
-      for (int p = 0; p < HP; ++p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            hr, LOPA_LDS(dst + WROWS * kRB + (4 * p + pw) * 1024), 16, hv[p], kc * kRB, 0, 0);
-    };
-    if (total > 0) {
+        for (int p = 0; p < HP; ++p)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              hr, LOPA_LDS(dst + WPX * 32 * kRB + (4 * p + pw) * 1024), 16, hv[p], kc * kRB, 0, 0);
+      };
 #pragma unroll
-      for (int u = 0; u < kStages - 1; ++u) issue(u);
-      wait_vmcnt<(kStages - 2) * (WP + HP)>();
+      for (int u = 0; u < S - 1; ++u) issue(u);
+      wait_vmcnt<(S - 2) * (WPX + HP)>();
       __builtin_amdgcn_s_barrier();
-      for (int i = 0; i + 1 < total; ++i) {
-        issue(i + kStages - 1);
-        wait_vmcnt<(kStages - 2) * (WP + HP)>();
+      for (int i = 0; i + 1 < cnt; ++i) {
+        issue(i + S - 1);
+        wait_vmcnt<(S - 2) * (WPX + HP)>();
         __builtin_amdgcn_s_barrier();
+      }
+      wait_vmcnt<0>();   // the next pipeline reuses the stages
+    };
+    if (total_a > 0)
+      pipeline(std::integral_constant<int, kStages>{}, std::integral_constant<int, WP>{}, 0,
+               total_a);
+    if constexpr (HAS_TAIL) {
+      if (total_b > 0) {
+        // the compute waves leave the full-width stages before the tail's
+        // first loads overwrite them
+        if (total_a > 0) __builtin_amdgcn_s_barrier();
+        pipeline(std::integral_constant<int, kTailStages>{}, std::integral_constant<int, TWP>{},
+                 total_a, total_b);
       }
     }
     wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
@@ -274,8 +303,8 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
-    auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NVW], u16x8 (&hf)[MTW])
-        __attribute__((always_inline)) {
+    auto frags = [&](const unsigned char* base, const unsigned char* hb, int j, u16x8 (&wf)[NVW],
+                     u16x8 (&hf)[MTW]) __attribute__((always_inline)) {
       const int s = j * 2 + lh;   // logical slot: K values 16j + 8lh .. +8
 #pragma unroll
       for (int n = 0; n < NVW; ++n) {
@@ -285,16 +314,17 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
         const int r = (wy * MTW + mt) * 32 + ln;
-        hf[mt] = *reinterpret_cast<const u16x8*>(base + (WROWS + r) * kRB + swz<kKC>(r, s) * 16);
+        hf[mt] = *reinterpret_cast<const u16x8*>(hb + r * kRB + swz<kKC>(r, s) * 16);
       }
     };
-    auto compute = [&](int b) __attribute__((always_inline)) {
-      const unsigned char* base = smem + b * BUF;
+    // base: the stage; hb: its activation rows (after the stage's weight rows)
+    auto compute = [&](const unsigned char* base, const unsigned char* hb)
+        __attribute__((always_inline)) {
       u16x8 wf[2][NVW], hf[2][MTW];
-      frags(base, 0, wf[0], hf[0]);
+      frags(base, hb, 0, wf[0], hf[0]);
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        if (j + 1 < KS) frags(base, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
+        if (j + 1 < KS) frags(base, hb, j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -337,18 +367,31 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
         for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
       }
     };
-    for (int i = 0; i < total; ++i) {
+    for (int i = 0; i < total_a; ++i) {
       __syncthreads();
-      // in the last, partial pass a wave column whose vocabulary tiles all
-      // lie past the range only keeps step (its logits would all be dropped).
-      // Only the 4-column bodies have such columns (a 594-row range ends 82
-      // rows into a 256-row pass); the 2-column ones run unconditionally.
+      // in a partial last pass a wave column whose vocabulary tiles all lie
+      // past the range only keeps step (its logits would all be dropped).
+      // Only the 4-column bodies have such columns; the 2-column ones run
+      // unconditionally.
+      const unsigned char* base = smem + (i % kStages) * BUF;
       if constexpr (WX == 4) {
-        if (v_lo + (i / nch) * WROWS + wx * (32 * NVW) < v_hi) compute(i % kStages);
+        if (v_lo + (i / nch) * WROWS + wx * (32 * NVW) < v_hi) compute(base, base + WROWS * kRB);
       } else {
-        compute(i % kStages);
+        compute(base, base + WROWS * kRB);
       }
       if (i % nch == nch - 1) finish_pass(i / nch);
+    }
+    if constexpr (HAS_TAIL) {
+      if (total_b > 0) {
+        if (total_a > 0) __syncthreads();   // done with the full-width stages
+        const bool live = wx * (32 * NVW) < rem;   // columns 0 and 1 only
+        for (int i = 0; i < total_b; ++i) {
+          __syncthreads();
+          const unsigned char* base = smem + (i % kTailStages) * TBUF;
+          if (live) compute(base, base + TROWS * kRB);
+        }
+        finish_pass(npass - 1);
+      }
     }
   }
   __syncthreads();

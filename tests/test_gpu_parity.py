@@ -177,6 +177,13 @@ HEAD_CASES = [
     # 300 rows: three row groups of <= 4 tiles; 450 rows: two groups of <= 8 tiles
     ("bf16-three-groups", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=2500, B=32, m=30, k=9), None),
     ("bf16-two-wide-groups", dict(dtype="bf16", Hq=2, Hkv=2, d=128, V=1900, B=64, m=50, k=8), None),
+    # vocabulary parts of 316, 384 and 448 rows (256 parts): a last pass of 60
+    # and of 128 rows runs as the half-width tail pipeline after a full pass;
+    # one of 192 rows stays in the full-width pipeline with idle columns
+    ("bf16-vocab-tail-60", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=80896, B=16, m=10, k=1), None),
+    ("bf16-vocab-tail-128", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=98304, B=16, m=10, k=1), None),
+    ("bf16-vocab-no-tail-192", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=114688, B=16, m=10, k=1),
+     None),
 ]
 
 
