@@ -13,7 +13,7 @@
 // streams the same number of weight bytes however N and K fall, and each
 // workgroup writes float32 partial tiles that the consumer kernels sum.
 // Inside a workgroup the machinery is the LM head's: four producer waves move
-// W and X chunks straight into a three-stage XOR-swizzled LDS ring with
+// W and X chunks straight into a three- or four-stage XOR-swizzled LDS ring with
 // buffer loads that write LDS, eight compute waves read
 // v_mfma_f32_32x32x16_bf16 fragments from it.  The activation fragment is the
 // MFMA's A operand, so a lane's outputs run along one weight row and the
