@@ -10,13 +10,15 @@
 // stored: a query row's branch follows from its index, and the kernel only
 // ever visits the prefix keys and that branch's block keys.
 //
-//   k_attn_dma    bf16, d = 128.  A workgroup takes 128 query rows of one KV
+//   k_attn_dma    bf16, d = 128.  A workgroup takes 64 query rows of one KV
 //                 head -- rows are (branch, position, q-head of the group), so
 //                 they span several positions and at most a few branches --
 //                 and walks 64-key work units: the committed prefix, then the
 //                 own block of each branch its rows belong to.  Four producer
 //                 waves move K and V rows into a three-stage LDS ring with
-//                 buffer-to-LDS loads; four compute waves take 32 rows each:
+//                 buffer-to-LDS loads; four compute waves take 32 rows and
+//                 one 32-key half of every unit each, and the two halves of
+//                 a row tile are merged through LDS at the end:
 //                 S^T = K Q^T and O^T = V^T P^T as v_mfma_f32_32x32x16_bf16
 //                 (V^T through transposing LDS reads), online softmax in
 //                 float32, P entering PV as a bf16 hi + lo pair so the
@@ -36,7 +38,7 @@ namespace lopa {
 // ---------------------------------------------------------------------------
 
 constexpr int kAD = 128;          // head dim
-constexpr int kARows = 128;       // query rows per workgroup (4 compute waves x 32)
+constexpr int kARows = 64;        // query rows per workgroup (2 row tiles x 2 key halves)
 // ---------------------------------------------------------------------------
 // MFMA path with buffer-to-LDS staging
 // ---------------------------------------------------------------------------
@@ -67,15 +69,17 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
 
 #define LOPA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// One workgroup: 128 query rows (branch, position, q-head of the group) of
+// One workgroup: 64 query rows (branch, position, q-head of the group) of
 // KV head g, and the work units [u_lo, u_hi) of its split -- units are the
 // 64-key blocks of the committed prefix followed by the own blocks of every
 // branch its rows belong to (a row only scores its own branch's block).
 // Waves 4..7 move K and V rows of a unit straight into an XOR-swizzled
-// three-stage LDS ring with buffer-to-LDS loads; waves 0..3 each own 32
-// query rows: S^T = K Q^T and O^T = V^T P^T as v_mfma_f32_32x32x16_bf16,
-// K fragments read in the kperm order, V^T fragments with transposing LDS
-// reads, online softmax in float32, P entering PV as a bf16 hi + lo pair.
+// three-stage LDS ring with buffer-to-LDS loads; wave w < 4 owns 32 query
+// rows (w & 1) and 32 keys of every unit (w >> 1): S^T = K Q^T and
+// O^T = V^T P^T as v_mfma_f32_32x32x16_bf16, K fragments read in the kperm
+// order, V^T fragments with transposing LDS reads, online softmax in
+// float32, P entering PV as a bf16 hi + lo pair; the two key halves of a
+// row tile keep separate softmax states, merged through LDS at the end.
 __global__ void __launch_bounds__(512)
 k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
            const int32_t* __restrict__ nb_ptr, const unsigned short* __restrict__ Kp,
@@ -155,14 +159,21 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
         __builtin_amdgcn_s_barrier();
       }
     }
-    attn_wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+    attn_wait_vmcnt<0>();   // no load may still target LDS when the ring is reused
+    // the two barriers of the key-half merge below
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();
     return;
   }
 
   // ---------------- compute waves ----------------
+  // wave w: row tile rt = w & 1 (32 query rows), key half kh = w >> 1 (keys
+  // 32 kh .. 32 kh + 31 of every unit); the two halves of a row tile keep
+  // their own online softmax and are merged through LDS at the end
+  const int rt = w & 1, kh = w >> 1;
   const int ln = lane & 31;     // this lane's query row within the wave's 32
   const int lh = lane >> 5;
-  const int grow = r0 + 32 * w + ln;
+  const int grow = r0 + 32 * rt + ln;
   const bool row_ok = grow < R;
   const int row = min(grow, R - 1);
   const int rbr = row / RB;                    // branch of the row
@@ -196,26 +207,32 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
                        : min(kAUnitKeys, L - u * kAUnitKeys);
     // rows of another branch see nothing of this branch's own block
     const bool see = !own || rbr == b_lo + v / obp;
-    // S^T = K Q^T, two 32-key tiles; all 16 K fragments go out first and the
-    // two tiles' accumulation chains interleave
-    u16x8 kf[2][8];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int kr = 32 * t + kperm(ln);
+    // whether any score of this half needs masking (keys past kn, another
+    // branch's block); decided before the MFMAs so that no branch sits
+    // between them and the first use of their results
+    const bool need_mask = __builtin_amdgcn_readfirstlane(kn) < 32 * kh + 32 ||
+                           __builtin_amdgcn_ballot_w64(!see) != 0;
+    // S^T = K Q^T over this wave's 32 keys: all 8 K fragments go out first,
+    // and the K = 128 sum runs as two interleaved chains added at the end
+    u16x8 kf[8];
+    {
+      const int kr = 32 * kh + kperm(ln);
       const unsigned char* kb = Ks + kr * kARowBytes;
       const int sw = aswz(kr);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        kf[t][s] = *reinterpret_cast<const u16x8*>(kb + (((2 * s + lh) ^ sw) << 4));
+        kf[s] = *reinterpret_cast<const u16x8*>(kb + (((2 * s + lh) ^ sw) << 4));
     }
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 sa = f32x16{}, sb = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[t][s]),
-                                                        __builtin_bit_cast(bf16x8, qf[s]), sc[t],
-                                                        0, 0, 0);
+    for (int s = 0; s < 8; s += 2) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]),
+                                                   __builtin_bit_cast(bf16x8, qf[s]), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s + 1]),
+                                                   __builtin_bit_cast(bf16x8, qf[s + 1]), sb, 0, 0,
+                                                   0);
+    }
+    const f32x16 sc = sa + sb;
     // V^T fragments of one 16-key PV step: [u2][half]
     auto vload = [&](int tp, bf16x4 (&va)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -231,23 +248,22 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
         }
     };
     bf16x4 va[2][4][2];
-    vload(0, va[0]);   // in flight during the softmax arithmetic
-    // sc[t][r] = raw score of key 32t + 16(r/8) + 8lh + r%8; keys past kn and
+    vload(2 * kh, va[0]);   // in flight during the softmax arithmetic
+    // sc[r] = raw score of key 32kh + 16(r/8) + 8lh + r%8; keys past kn and
     // other branches' own blocks are masked (wave-uniform test first)
-    if (__builtin_amdgcn_readfirstlane(kn) < kAUnitKeys || __builtin_amdgcn_ballot_w64(!see) != 0) {
+    float scm[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int r = 0; r < 16; ++r) scm[r] = sc[r];
+    if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + 16 * (r >> 3) + 8 * lh + (r & 7);
-          if (!(see && key < kn)) sc[t][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kh + 16 * (r >> 3) + 8 * lh + (r & 7);
+        if (!(see && key < kn)) scm[r] = -INFINITY;
+      }
     }
     float bmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sc[t][r]);
+    for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, scm[r]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave)) * scale2;
     // The exponent reference m_ref (log2 units) only moves when a row's block
     // maximum exceeds it by more than 8, so p <= 2^8 and the rescale of O and
@@ -263,13 +279,13 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
     }
     // a row that has seen no key yet keeps m_ref = -inf and all p = 0
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    // P^T operands of the four 16-key PV steps, as bf16 hi + lo
-    bf16x8 phi[4], plo[4];
+    // P^T operands of this half's two 16-key PV steps, as bf16 hi + lo
+    bf16x8 phi[2], plo[2];
 #pragma unroll
-    for (int tp = 0; tp < 4; ++tp)
+    for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[tp >> 1][8 * (tp & 1) + e], scale2, -m_use));
+        const float p = __builtin_amdgcn_exp2f(fmaf(scm[8 * tp + e], scale2, -m_use));
         l_run += p;
         const bf16 hi = static_cast<bf16>(p);
         phi[tp][e] = hi;
@@ -277,8 +293,8 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
       }
     // O^T += V^T P^T; the next step's V^T fragments are read during this one's MFMAs
 #pragma unroll
-    for (int tp = 0; tp < 4; ++tp) {
-      if (tp < 3) vload(tp + 1, va[(tp + 1) & 1]);
+    for (int tp = 0; tp < 2; ++tp) {
+      if (tp < 1) vload(2 * kh + tp + 1, va[(tp + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u2 = 0; u2 < 4; ++u2) {
@@ -289,6 +305,34 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // ---- merge of the two key halves of each row tile, through the ring ----
+  // (the producers' last loads have landed before the first barrier)
+  float* xo = reinterpret_cast<float*>(smem) + rt * (64 * 64);        // [j][lane]
+  float* xm = reinterpret_cast<float*>(smem) + 2 * (64 * 64) + rt * 128;  // m, then l
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(16 * u2 + r) * 64 + lane] = o[u2][r];
+    xm[lane] = m_ref;
+    xm[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float M = fmaxf(m_ref, m1);
+    const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[u2][r] = o[u2][r] * a0 + xo[(16 * u2 + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_ref = M;
   }
 
   // ---- output: o[u][r] = O[row ln][dim 32u + 8(r/4) + 4lh + r%4] ----

@@ -9,15 +9,18 @@
 
 namespace lopa {
 
-// Attention MFMA kernel (bf16, d = 128): workgroups of 128 query rows per KV
+// Attention MFMA kernel (bf16, d = 128): workgroups of 64 query rows per KV
 // head walk work units of 64 keys -- the committed prefix in blocks, then the
-// own block of every branch their rows belong to.  When one pass leaves most
-// compute units idle the units are split over grid.z (at most one workgroup
-// per compute unit, at least two units per split, at most kAttnMaxSplits)
-// and a second kernel merges the splits' unnormalised partials.
-constexpr int kAttnRowsPerWG = 128;
+// own block of every branch their rows belong to.  The units may be split
+// over grid.z (at most one workgroup per compute unit, at least two units per
+// split, at most kAttnMaxSplits), and a second kernel then merges the splits'
+// unnormalised partials; that merge costs about kAttnSplitCostUnits units of
+// one workgroup's time, so the split count minimises
+// ceil(units / splits) + (splits > 1) * kAttnSplitCostUnits.
+constexpr int kAttnRowsPerWG = 64;
 constexpr int kAttnKeysPerBlock = 64;
 constexpr int kAttnMaxSplits = 16;
+constexpr int kAttnSplitCostUnits = 8;
 
 struct AttnPlan {
   bool mfma;
@@ -35,10 +38,18 @@ inline AttnPlan attn_plan(const lopa_dims& d) {
   const int wgs = p.row_groups * d.Hkv;
   const int units = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock +
                     (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
-  int s = 256 / wgs;
-  if (s > units / 2) s = units / 2;
-  if (s > kAttnMaxSplits) s = kAttnMaxSplits;
-  p.splits = s < 1 ? 1 : s;
+  int smax = 256 / wgs;
+  if (smax > units / 2) smax = units / 2;
+  if (smax > kAttnMaxSplits) smax = kAttnMaxSplits;
+  p.splits = 1;
+  int best = units;
+  for (int s = 2; s <= smax; ++s) {
+    const int t = (units + s - 1) / s + kAttnSplitCostUnits;
+    if (t < best) {
+      best = t;
+      p.splits = s;
+    }
+  }
   return p;
 }
 

@@ -116,13 +116,16 @@ class ModelDecodeBuffers:
 
 
 def model_decode_block(model: Model, dims, k: int, tau: float, tok0, buf: ModelDecodeBuffers,
-                       steps: int, log=None, stream=None) -> None:
+                       steps: int, log=None, stream=None, state_log=None) -> None:
     """Decode one block with the model: the initial pass (the block as it
     stands in slot 0, the LM head on its masked positions), then ``steps``
     verification steps, each build -> forward -> LM head -> select with the
     winner's state swapped in.  ``dims`` carries the current prefix length
     (dims.L rows of the model's cache are the committed prefix).  ``log``
-    (device int32 [steps][B]) receives the tokens after each step."""
+    (device int32 [steps][B]) receives the tokens after each step;
+    ``state_log`` (device float32 and int32 tensors [steps + 1][B]) the
+    confidences and tokens of the state: row 0 after the initial pass, row
+    s + 1 after step s."""
     import numpy as np
     import torch
     from . import MASK
@@ -144,6 +147,9 @@ def model_decode_block(model: Model, dims, k: int, tau: float, tok0, buf: ModelD
                      s.arg, None, s.ws, stream)
     buf.conf.copy_(s.conf[:B])
     buf.arg.copy_(s.arg[:B])
+    if state_log is not None:
+        state_log[0][0].copy_(buf.conf)
+        state_log[1][0].copy_(buf.arg)
     for i in range(steps):
         lopa_branch_build(dims, k, tau, buf.tok, buf.conf, buf.arg, s.nb, s.br_tok, s.br_mask,
                           s.rows, s.row_ptr, stream)
@@ -155,15 +161,19 @@ def model_decode_block(model: Model, dims, k: int, tau: float, tok0, buf: ModelD
         buf.swap_state()
         if log is not None:
             log[i].copy_(buf.tok)
+        if state_log is not None:
+            state_log[0][i + 1].copy_(buf.conf)
+            state_log[1][i + 1].copy_(buf.arg)
 
 
 def model_decode_sequence(model: Model, k: int, tau: float, blocks, buf: ModelDecodeBuffers,
-                          logs=None, stream=None) -> int:
+                          logs=None, stream=None, state_logs=None) -> int:
     """Decode ``blocks`` one after another with the model, committing each
     decoded block's winner K/V of every layer (lopa_model_commit) at the end
     of the prefix, so the next block attends to it.  The model's cache must
-    have room for the prefix plus len(blocks) * B rows.  Returns the final
-    prefix length."""
+    have room for the prefix plus len(blocks) * B rows.  ``logs`` /
+    ``state_logs`` hold one model_decode_block log / state_log per block.
+    Returns the final prefix length."""
     import numpy as np
     from . import MASK, Dims, lopa_model_commit
     import torch
@@ -175,7 +185,7 @@ def model_decode_sequence(model: Model, k: int, tau: float, blocks, buf: ModelDe
                   dtype=d0.dtype)
         m = int(np.sum(np.asarray(tok0) == MASK))
         model_decode_block(model, dj, k, tau, tok0, buf, m, None if logs is None else logs[j],
-                           stream)
+                           stream, None if state_logs is None else state_logs[j])
         # with no step taken, slot 0 holds the block (written by the initial pass)
         lopa_model_commit(dj, model.md, buf.step.winner if m else zero, buf.fwd.Kb, buf.fwd.Vb,
                           model.Kp, model.Vp, model.kv_rows, L, stream)

@@ -323,26 +323,19 @@ def forward(seed: int, cfg: ModelCfg, L: int, br_tok: np.ndarray, layers=None,
 # Decoding blocks with the model
 # ---------------------------------------------------------------------------
 
-def decode_block(seed: int, cfg: ModelCfg, L: int, tok0, k: int, tau: float, nb_max: int,
-                 layers=None, prefix=None, max_steps: int | None = None):
-    """Decode tok0's masked positions with the model: the initial pass (the
-    block alone through the model, the LM head on its masked positions),
-    then verification steps -- explore (lopa_oracle.branch_build), every
-    branch through the model, the LM head on the still-masked rows, select
-    and reuse -- until none is masked (news article, section "LoPA 的核心设计：
-    前瞻并行与分支验证"; the LM head weight is the model's).  Returns the trace
-    (decode_oracle.DecodeTrace) and the winner's block keys and values of
-    every layer from the last pass ([n_layers][B][Hkv][d] each), the cache a
-    commit appends."""
-    from .decode_oracle import DecodeStep, DecodeTrace, _explore_gaps
-    from .lopa_oracle import branch_build, branch_select, lmhead_conf
-    if layers is None:
-        layers = [synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
-    if prefix is None:
-        prefix = [synth_prefix(seed, cfg, l, L) for l in range(cfg.n_layers)]
-    W = synth_rows(seed, cfg, TENSOR_ID["lm_head"], np.arange(cfg.V)).astype(np.float32)
-    B = len(tok0)
-    tok = np.asarray(tok0, np.int32).copy()
+def lm_head_weight(seed: int, cfg: ModelCfg) -> np.ndarray:
+    """The model's LM head [V][hidden] (bf16 values)."""
+    return synth_rows(seed, cfg, TENSOR_ID["lm_head"], np.arange(cfg.V)).astype(np.float32)
+
+
+def initial_pass(seed: int, cfg: ModelCfg, L: int, tok, layers, prefix, W):
+    """The block as it stands through the model and the LM head on its masked
+    positions.  Returns (conf [B] float32, arg [B] int32, margin [B]: the
+    top-2 logit gap behind each masked position's token, inf elsewhere,
+    the forward's output)."""
+    from .lopa_oracle import lmhead_conf
+    tok = np.asarray(tok, np.int32)
+    B = len(tok)
     out = forward(seed, cfg, L, tok[None], layers, prefix)
     masked = np.flatnonzero(tok == MASK)
     head = lmhead_conf(out.H[0, masked, :], W)
@@ -352,35 +345,71 @@ def decode_block(seed: int, cfg: ModelCfg, L: int, tok0, k: int, tau: float, nb_
     arg[masked] = head.arg
     margin = np.full(B, np.inf)
     margin[masked] = head.margin
+    return conf, arg, margin, out
+
+
+def decode_step(seed: int, cfg: ModelCfg, L: int, tok, conf, arg, margin, k: int, tau: float,
+                nb_max: int, layers, prefix, W):
+    """One verification step with the model from the state (tok, conf, arg):
+    explore (lopa_oracle.branch_build), every branch through the model, the
+    LM head on the still-masked rows, select and reuse.  ``margin`` [B] is
+    the top-2 logit gap behind each masked position's arg.  Returns
+    (decode_oracle.DecodeStep, the next (tok, conf, arg, margin), the
+    forward's output, the winner, the branches (lopa_oracle.Branches) and
+    the top-2 logit gap of every LM-head row [nb_max * B], inf elsewhere)."""
+    from .decode_oracle import DecodeStep, _explore_gaps
+    from .lopa_oracle import branch_build, branch_select, lmhead_conf
+    B = len(tok)
+    rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k)
+    br = branch_build(tok, conf, arg, k, np.float32(tau), nb_max)
+    out = forward(seed, cfg, L, br.br_tok[:br.nb], layers, prefix)
+    rows = np.asarray(br.rows)
+    n = nb_max * B
+    conf_pos, arg_pos, margin_pos = np.zeros(n), np.full(n, -1), np.full(n, np.inf)
+    if rows.size:
+        h = lmhead_conf(np.stack([out.H[r // B, r % B] for r in rows]), W)
+        conf_pos[rows], arg_pos[rows], margin_pos[rows] = h.conf, h.arg, h.margin
+    sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
+    bc = np.sort(np.asarray(sel.bconf[:br.nb], np.float64))[::-1]
+    new_tok = np.asarray(sel.tok_next, np.int32)
+    filled = (tok == MASK) & (new_tok != MASK)
+    w = int(sel.winner)
+    step = DecodeStep(br.nb, w, new_tok.copy(), int(filled.sum()),
+                      float(margin[filled].min()) if filled.any() else np.inf,
+                      rank_gap, tau_gap, float(bc[0] - bc[1]) if bc.size > 1 else np.inf)
+    nxt = (new_tok, np.asarray(sel.conf_next, np.float32), np.asarray(sel.arg_next, np.int32),
+           np.where(new_tok == MASK, margin_pos[w * B:(w + 1) * B], np.inf))
+    return step, nxt, out, w, br, margin_pos
+
+
+def decode_block(seed: int, cfg: ModelCfg, L: int, tok0, k: int, tau: float, nb_max: int,
+                 layers=None, prefix=None, max_steps: int | None = None):
+    """Decode tok0's masked positions with the model: the initial pass (the
+    block alone through the model, the LM head on its masked positions),
+    then verification steps (decode_step) until none is masked (news
+    article, section "LoPA 的核心设计：前瞻并行与分支验证"; the LM head weight
+    is the model's).  Returns the trace (decode_oracle.DecodeTrace) and the
+    winner's block keys and values of every layer from the last pass
+    ([n_layers][B][Hkv][d] each), the cache a commit appends."""
+    from .decode_oracle import DecodeTrace
+    if layers is None:
+        layers = [synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
+    if prefix is None:
+        prefix = [synth_prefix(seed, cfg, l, L) for l in range(cfg.n_layers)]
+    W = lm_head_weight(seed, cfg)
+    tok = np.asarray(tok0, np.int32).copy()
+    conf, arg, margin, out = initial_pass(seed, cfg, L, tok, layers, prefix, W)
+    masked = np.isfinite(margin)
     tr = DecodeTrace(tok.copy(), conf.copy(), arg.copy(),
-                     float(head.margin.min()) if head.margin.size else np.inf)
+                     float(margin[masked].min()) if masked.any() else np.inf)
     Kw, Vw = out.Kb[:, 0], out.Vb[:, 0]
-    limit = int(masked.size) if max_steps is None else max_steps
+    limit = int(np.sum(tok == MASK)) if max_steps is None else max_steps
     for _ in range(limit):
         if not np.any(tok == MASK):
             break
-        rank_gap, tau_gap = _explore_gaps(tok, conf, np.float64(np.float32(tau)), k)
-        br = branch_build(tok, conf, arg, k, np.float32(tau), nb_max)
-        out = forward(seed, cfg, L, br.br_tok[:br.nb], layers, prefix)
-        rows = np.asarray(br.rows)
-        n = nb_max * B
-        conf_pos, arg_pos, margin_pos = np.zeros(n), np.full(n, -1), np.full(n, np.inf)
-        if rows.size:
-            h = lmhead_conf(np.stack([out.H[r // B, r % B] for r in rows]), W)
-            conf_pos[rows], arg_pos[rows], margin_pos[rows] = h.conf, h.arg, h.margin
-        sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
-        bc = np.sort(np.asarray(sel.bconf[:br.nb], np.float64))[::-1]
-        new_tok = np.asarray(sel.tok_next, np.int32)
-        filled = (tok == MASK) & (new_tok != MASK)
-        tr.steps.append(DecodeStep(br.nb, int(sel.winner), new_tok.copy(), int(filled.sum()),
-                                   float(margin[filled].min()) if filled.any() else np.inf,
-                                   rank_gap, tau_gap,
-                                   float(bc[0] - bc[1]) if bc.size > 1 else np.inf))
-        w = int(sel.winner)
-        margin = np.where(new_tok == MASK, margin_pos[w * B:(w + 1) * B], np.inf)
-        tok = new_tok
-        conf = np.asarray(sel.conf_next, np.float32)
-        arg = np.asarray(sel.arg_next, np.int32)
+        st, (tok, conf, arg, margin), out, w, _, _ = decode_step(
+            seed, cfg, L, tok, conf, arg, margin, k, tau, nb_max, layers, prefix, W)
+        tr.steps.append(st)
         Kw, Vw = out.Kb[:, w], out.Vb[:, w]
     return tr, Kw, Vw
 

@@ -103,24 +103,26 @@ def test_null_pointers_and_k_rejected():
 def test_workspace_size_and_shortfall():
     d = _dims()
     need = lopa.workspace_bytes(d)
-    # prefix 512 = 8 key blocks + 1 own block, 9 row groups x 4 KV heads = 36
-    # workgroups: min(256 // 36, 9 // 2) = 4 splits of attention partials
-    # (O, max, sum = 130 floats per row) dominate the LM head's partials
-    assert need == 4 * 4 * (5 * 32 * 7) * 130 * 4
-    assert lopa.workspace_bytes(_dims(k_max=8)) == 4 * 4 * (9 * 32 * 7) * 130 * 4
-    # a long prefix: 16 row groups x 4 heads = 128 workgroups -> 2 splits
-    split = _dims(L=4096, B=64, k_max=8)
-    assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 64 * 7) * 130 * 4
-    # the LM head alone needs rows x 256 vocabulary parts x (max, sum, argmax,
+    # the LM head needs rows x 256 vocabulary parts x (max, sum, argmax,
     # entropy term or perturbed score, sampled logit)
     head_need = 5 * 32 * 256 * 20
+    # prefix 512 = 8 key blocks + 1 own block over 18 row groups x 4 KV heads:
+    # a split would cost more than its 9 units, so attention needs no partials
+    assert need == head_need
+    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 20
+    assert lopa.workspace_bytes(_dims(L=4096, B=64, k_max=8)) == 9 * 64 * 256 * 20
+    # prefix 2048: 33 units over 32 row groups x 4 heads = 128 workgroups ->
+    # 2 splits (17 + 8 < 33) of attention partials (O, max, sum = 130 floats
+    # per row), which then dominate
+    split = _dims(L=2048, k_max=8)
+    assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 32 * 7) * 130 * 4
     fake = ctypes.c_void_p(16)
     L = lopa.lib()
     args = [fake] * 8
     assert L.lopa_lmhead_conf(ctypes.byref(d), *args, fake, head_need - 1, None) == -3
     assert L.lopa_lmhead_conf(ctypes.byref(d), *args, None, need, None) == -3
-    assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
-                              need - 1, None) == -3
+    assert L.lopa_branch_attn(ctypes.byref(split), fake, fake, fake, fake, fake, fake, fake,
+                              fake, lopa.workspace_bytes(split) - 1, None) == -3
     f32 = _dims(dtype=lopa.F32, V=1000)
     assert lopa.workspace_bytes(f32) == 5 * 32 * 4 * 20
 

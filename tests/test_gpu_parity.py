@@ -161,6 +161,26 @@ def test_gpu_attn(name, ov, nb):
     assert np.all(Hg[nb:] == 7.0)
 
 
+@pytest.mark.parametrize("kn", [1, 8, 15, 16, 23, 24, 27, 28, 31, 32, 33, 40, 47, 48, 55, 56, 63])
+def test_gpu_attn_ragged_last_unit(kn):
+    """Every way a prefix can end inside a 64-key unit: kn valid keys in the
+    last one, so each 32-key half of it holds none, some or all of them (a
+    toolchain hazard once corrupted exactly the kn = 24..31 and 56..63
+    cases)."""
+    ov = dict(dtype="bf16", L=64 + kn, B=16, m=8, Hq=4, Hkv=1, d=128, k=2)
+    inp = synth.make_inputs(synth.TINY, with_weight=False, **ov)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    x = device_inputs(inp)
+    buf = StepBuffers(dims)
+    nb = dims.nb_max
+    lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"],
+                          to_device(np.array([nb], np.int32)), buf.H, buf.ws)
+    torch.cuda.synchronize()
+    Hx = O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv)
+    assert_h_close(act_to_f64(buf.H)[:nb], Hx[:nb], cfg.dtype, f"kn={kn}")
+
+
 # ---------------------------------------------------------------------------
 # LM head (per call, identical inputs: the oracle's rounded H)
 # ---------------------------------------------------------------------------
