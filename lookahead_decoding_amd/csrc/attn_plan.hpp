@@ -14,13 +14,13 @@ namespace lopa {
 // own block of every branch their rows belong to.  The units may be split
 // over grid.z (at most one workgroup per compute unit, at least two units per
 // split, at most kAttnMaxSplits), and a second kernel then merges the splits'
-// unnormalised partials; that merge costs about kAttnSplitCostUnits units of
-// one workgroup's time, so the split count minimises
+// unnormalised partials; that merge (with its launch) costs about
+// kAttnSplitCostUnits units of one workgroup's time, so the split count minimises
 // ceil(units / splits) + (splits > 1) * kAttnSplitCostUnits.
 constexpr int kAttnRowsPerWG = 64;
 constexpr int kAttnKeysPerBlock = 64;
 constexpr int kAttnMaxSplits = 16;
-constexpr int kAttnSplitCostUnits = 8;
+constexpr int kAttnSplitCostUnits = 5;
 
 struct AttnPlan {
   bool mfma;

@@ -106,14 +106,15 @@ def test_workspace_size_and_shortfall():
     # the LM head needs rows x 256 vocabulary parts x (max, sum, argmax,
     # entropy term or perturbed score, sampled logit)
     head_need = 5 * 32 * 256 * 20
-    # prefix 512 = 8 key blocks + 1 own block over 18 row groups x 4 KV heads:
-    # a split would cost more than its 9 units, so attention needs no partials
-    assert need == head_need
+    # prefix 512 = 8 key blocks + 1 own block over 18 row groups x 4 KV heads
+    # = 72 workgroups: 3 splits (3 units + the merge's 5 < 9) of attention
+    # partials (O, max, sum = 130 floats per row), which dominate
+    assert need == 3 * 4 * (5 * 32 * 7) * 130 * 4
+    # 9 branches: 128 workgroups leave room for 2 splits, which would not pay
     assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 20
     assert lopa.workspace_bytes(_dims(L=4096, B=64, k_max=8)) == 9 * 64 * 256 * 20
     # prefix 2048: 33 units over 32 row groups x 4 heads = 128 workgroups ->
-    # 2 splits (17 + 8 < 33) of attention partials (O, max, sum = 130 floats
-    # per row), which then dominate
+    # 2 splits (17 + 5 < 33)
     split = _dims(L=2048, k_max=8)
     assert lopa.workspace_bytes(split) == 2 * 4 * (9 * 32 * 7) * 130 * 4
     fake = ctypes.c_void_p(16)
