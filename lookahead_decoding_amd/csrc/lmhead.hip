@@ -334,38 +334,42 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
                 acc[mt][n], 0, 0, 0);
       }
     };
+    // Fold the logits of one activation row tile -- tiles a[0 .. NV) of 32
+    // vocabulary entries from vb on, row r -- into the running partial of
+    // vocabulary column col, and clear the tiles.
+    auto fold = [&](auto& a, int vb, int col, int r) __attribute__((always_inline)) {
+      constexpr int NV = static_cast<int>(sizeof(a) / sizeof(a[0]));
+      RP p;
+      if constexpr (MODE == kModeSample) {
+        const unsigned pos = static_cast<unsigned>(rows[row0 + min(r, Mg - 1)] % smp.B);
+        p = row_partial_sample<NV>(a, vb, lh, v_hi, smp, pos);
+      } else {
+        p = row_partial<NV, ENT>(a, vb, lh, v_hi);
+      }
+      if (lh == 0) {
+        RP q = merge(run[col * RUNS + r], p);
+        if constexpr (MODE == kModeConf) q.t = 0.f;   // keeps the entropy arithmetic out
+        run[col * RUNS + r] = q;
+      }
+      if (logits_out && r < Mg) {
+        const size_t lb = static_cast<size_t>(rows[row0 + r]) * V;
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int v = vb + n * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
+            if (v < v_hi) logits_out[lb + v] = a[n][q];
+          }
+      }
+#pragma unroll
+      for (int n = 0; n < NV; ++n) a[n] = f32x16{};
+    };
     // acc[mt][n][q] = logit of row (wy*MTW + mt)*32 + ln, vocabulary entry
     // vbw + 32n + 8(q/4) + 4lh + q%4
     auto finish_pass = [&](int pass) {
-      const int vbw = v_lo + pass * WROWS + wx * (32 * NVW);
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
-        const int r = (wy * MTW + mt) * 32 + ln;
-        RP p;
-        if constexpr (MODE == kModeSample) {
-          const unsigned pos = static_cast<unsigned>(rows[row0 + min(r, Mg - 1)] % smp.B);
-          p = row_partial_sample<NVW>(acc[mt], vbw, lh, v_hi, smp, pos);
-        } else {
-          p = row_partial<NVW, ENT>(acc[mt], vbw, lh, v_hi);
-        }
-        if (lh == 0) {
-          RP q = merge(run[wx * RUNS + r], p);
-          if constexpr (MODE == kModeConf) q.t = 0.f;   // keeps the entropy arithmetic out
-          run[wx * RUNS + r] = q;
-        }
-        if (logits_out && r < Mg) {
-          const size_t lb = static_cast<size_t>(rows[row0 + r]) * V;
-#pragma unroll
-          for (int n = 0; n < NVW; ++n)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int v = vbw + n * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
-              if (v < v_hi) logits_out[lb + v] = acc[mt][n][q];
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NVW; ++n) acc[mt][n] = f32x16{};
-      }
+      for (int mt = 0; mt < MTW; ++mt)
+        fold(acc[mt], v_lo + pass * WROWS + wx * (32 * NVW), wx, (wy * MTW + mt) * 32 + ln);
     };
     for (int i = 0; i < total_a; ++i) {
       __syncthreads();
@@ -384,13 +388,44 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     if constexpr (HAS_TAIL) {
       if (total_b > 0) {
         if (total_a > 0) __syncthreads();   // done with the full-width stages
-        const bool live = wx * (32 * NVW) < rem;   // columns 0 and 1 only
+        // In the tail every wave takes one 32-row weight tile tw = w / 2
+        // against the activation tiles of row group ty = w mod 2, so the
+        // live tiles (rem <= 128 rows) are spread over all eight waves; the
+        // accumulators acc[mt][0] hold them (acc[mt][1] stays zero).
+        static_assert(NVW == 2 && T::WY == 2, "tail layout");
+        const int tw = w >> 1, ty = w & 1;
+        const bool live = tw * 32 < rem;
+        const int wr = tw * 32 + ln;
         for (int i = 0; i < total_b; ++i) {
           __syncthreads();
+          if (!live) continue;
           const unsigned char* base = smem + (i % kTailStages) * TBUF;
-          if (live) compute(base, base + TROWS * kRB);
+          const unsigned char* hb = base + TROWS * kRB;
+          u16x8 wf[2], hf[2][MTW];
+          auto tfrags = [&](int j, u16x8& wv, u16x8 (&hv)[MTW]) __attribute__((always_inline)) {
+            const int sl = j * 2 + lh;
+            wv = *reinterpret_cast<const u16x8*>(base + wr * kRB + swz<kKC>(wr, sl) * 16);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+              const int r = (ty * MTW + mt) * 32 + ln;
+              hv[mt] = *reinterpret_cast<const u16x8*>(hb + r * kRB + swz<kKC>(r, sl) * 16);
+            }
+          };
+          tfrags(0, wf[0], hf[0]);
+#pragma unroll
+          for (int j = 0; j < KS; ++j) {
+            if (j + 1 < KS) tfrags(j + 1, wf[(j + 1) & 1], hf[(j + 1) & 1]);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+              acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, wf[j & 1]), __builtin_bit_cast(bf16x8, hf[j & 1][mt]),
+                  acc[mt][0], 0, 0, 0);
+          }
         }
-        finish_pass(npass - 1);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+          fold(*reinterpret_cast<f32x16(*)[1]>(&acc[mt][0]),
+               v_lo + (npass - 1) * WROWS + tw * 32, tw, (ty * MTW + mt) * 32 + ln);
       }
     }
   }
