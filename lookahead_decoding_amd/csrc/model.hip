@@ -191,7 +191,7 @@ k_qkv_epilogue(GemmView v, const float* __restrict__ P, int B, int Hq, int Hkv, 
   const int hh = (idx / quads) % heads;
   const int r = idx / (quads * heads);
   const int ni = hh * d + i0, nj = ni + half;
-  const float4 pa = v.sum4(P, tab, r, ni), pb = v.sum4(P, tab, r, nj);
+  const float4 pa = v.sum4<8>(P, tab, r, ni), pb = v.sum4<8>(P, tab, r, nj);
   float a[4] = {pa.x, pa.y, pa.z, pa.w}, b[4] = {pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
