@@ -272,8 +272,8 @@ def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the step is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the verification step "
+              "runs on a single GPU and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 
