@@ -118,29 +118,41 @@ __device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], in
 // a[n][r] = logit of vocabulary entry vb + 32n + 8(r/4) + 4h + r%4 (the
 // 32x32 MFMA output layout, h = lane / 32), merged with the other lane half
 // that holds the same row.  ENT: also the entropy term t (else t = 0).
-template <int NV, bool ENT>
+//
+// Straight-line code: the max and its index move together by selects when
+// an entry is strictly larger (the entries ascend in this order, so the
+// lowest index keeps a tie).  MASKED: some entries may lie at or past vend
+// and are skipped; without it (every pass but a part's last) there is no
+// test at all.  exp2 is the hardware instruction: its argument
+// (l - max) log2 e is <= 0, and a term below 2^-126, which the hardware
+// flushes to zero, is far below half an ulp of a sum that holds the max's
+// own term 1.
+template <int NV, bool ENT, bool MASKED>
 __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, int h, int vend) {
   Partial p = empty_partial();
+  const int v0 = vb + 4 * h;
 #pragma unroll
   for (int n = 0; n < NV; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int v = vb + n * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (v < vend && a[n][r] > p.m) {
-        p.m = a[n][r];
-        p.i = v;
-      }
+      const int v = v0 + n * 32 + 8 * (r >> 2) + (r & 3);
+      const bool c = MASKED ? (v < vend) & (a[n][r] > p.m) : a[n][r] > p.m;
+      p.m = c ? a[n][r] : p.m;
+      p.i = c ? v : p.i;
     }
-  if (p.i != 0x7fffffff) {
+  if (!MASKED || p.i != 0x7fffffff) {
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = vb + n * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (v < vend) {
-          const float dl = a[n][r] - p.m;
-          const float e = exp2f(dl * kLog2e);
+        const float dl = a[n][r] - p.m;
+        const float e = __builtin_amdgcn_exp2f(dl * kLog2e);
+        if constexpr (MASKED) {
+          const bool ok = v0 + n * 32 + 8 * (r >> 2) + (r & 3) < vend;
+          s += ok ? e : 0.f;
+          if constexpr (ENT) t = ok ? fmaf(e, dl, t) : t;
+        } else {
           s += e;
           if constexpr (ENT) t = fmaf(e, dl, t);
         }
@@ -337,14 +349,15 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     // Fold the logits of one activation row tile -- tiles a[0 .. NV) of 32
     // vocabulary entries from vb on, row r -- into the running partial of
     // vocabulary column col, and clear the tiles.
-    auto fold = [&](auto& a, int vb, int col, int r) __attribute__((always_inline)) {
+    auto fold = [&](auto masked, auto& a, int vb, int col, int r) __attribute__((always_inline)) {
       constexpr int NV = static_cast<int>(sizeof(a) / sizeof(a[0]));
+      constexpr bool MASKED = decltype(masked)::value;
       RP p;
       if constexpr (MODE == kModeSample) {
         const unsigned pos = static_cast<unsigned>(rows[row0 + min(r, Mg - 1)] % smp.B);
         p = row_partial_sample<NV>(a, vb, lh, v_hi, smp, pos);
       } else {
-        p = row_partial<NV, ENT>(a, vb, lh, v_hi);
+        p = row_partial<NV, ENT, MASKED>(a, vb, lh, v_hi);
       }
       if (lh == 0) {
         RP q = merge(run[col * RUNS + r], p);
@@ -366,24 +379,33 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
     };
     // acc[mt][n][q] = logit of row (wy*MTW + mt)*32 + ln, vocabulary entry
     // vbw + 32n + 8(q/4) + 4lh + q%4
+    // A pass wholly inside the part folds without bound tests.
     auto finish_pass = [&](int pass) {
+      const int vb = v_lo + pass * WROWS + wx * (32 * NVW);
+      if (v_lo + (pass + 1) * WROWS <= v_hi) {
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-        fold(acc[mt], v_lo + pass * WROWS + wx * (32 * NVW), wx, (wy * MTW + mt) * 32 + ln);
+        for (int mt = 0; mt < MTW; ++mt)
+          fold(std::false_type{}, acc[mt], vb, wx, (wy * MTW + mt) * 32 + ln);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+          fold(std::true_type{}, acc[mt], vb, wx, (wy * MTW + mt) * 32 + ln);
+      }
     };
-    for (int i = 0; i < total_a; ++i) {
-      __syncthreads();
+    // One pass = nch chunks, then the fold.  The fold sits outside the
+    // chunk loop so the loop body holds nothing but the MFMA step.
+    for (int pass = 0, i = 0; pass * nch < total_a; ++pass) {
       // in a partial last pass a wave column whose vocabulary tiles all lie
       // past the range only keeps step (its logits would all be dropped).
       // Only the 4-column bodies have such columns; the 2-column ones run
       // unconditionally.
-      const unsigned char* base = smem + (i % kStages) * BUF;
-      if constexpr (WX == 4) {
-        if (v_lo + (i / nch) * WROWS + wx * (32 * NVW) < v_hi) compute(base, base + WROWS * kRB);
-      } else {
-        compute(base, base + WROWS * kRB);
+      const bool live = WX != 4 || v_lo + pass * WROWS + wx * (32 * NVW) < v_hi;
+      for (int c = 0; c < nch; ++c, ++i) {
+        __syncthreads();
+        const unsigned char* base = smem + (i % kStages) * BUF;
+        if (live) compute(base, base + WROWS * kRB);
       }
-      if (i % nch == nch - 1) finish_pass(i / nch);
+      finish_pass(pass);
     }
     if constexpr (HAS_TAIL) {
       if (total_b > 0) {
@@ -424,7 +446,7 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
         }
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
-          fold(*reinterpret_cast<f32x16(*)[1]>(&acc[mt][0]),
+          fold(std::true_type{}, *reinterpret_cast<f32x16(*)[1]>(&acc[mt][0]),
                v_lo + (npass - 1) * WROWS + tw * 32, tw, (ty * MTW + mt) * 32 + ln);
       }
     }
