@@ -60,9 +60,13 @@ struct Sampling {
   int B;
 };
 
+// Both logarithms take the hardware log2 (times ln 2): u >= 2^-24 and
+// -ln u >= 2^-24 are normal numbers, so no denormal scaling is needed, and
+// the result stays within a few ulp of the library logf's.
+constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float gumbel(unsigned x) {
   const float u = static_cast<float>(2u * (x >> 9) + 1u) * (1.f / 16777216.f);
-  return -logf(-logf(u));
+  return -kLn2 * __builtin_amdgcn_logf(-kLn2 * __builtin_amdgcn_logf(u));
 }
 
 // Sampling partial of one lane's logits for one LM-head row at block
