@@ -147,18 +147,35 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
       // store addresses are formed here and not kept live across the K loop
       int r0 = wy * MTW * 32 + 4 * lh;
       __asm__ volatile("" : "+v"(r0));
+      // A wave whose rows and columns all lie inside the unit's tile (every
+      // wave, unless M or N is ragged) stores without per-element tests:
+      // straight-line stores, not a branch around each one.
+      const bool inside = (wy * MTW + LIVE) * 32 <= mg && (wx * NVW + NVW) * 32 <= ng;
+      if (inside) {
 #pragma unroll
-      for (int mt = 0; mt < LIVE; ++mt)
+        for (int mt = 0; mt < LIVE; ++mt)
 #pragma unroll
-        for (int n = 0; n < NVW; ++n) {
-          const int c = (wx * NVW + n) * 32 + ln;
+          for (int n = 0; n < NVW; ++n) {
+            const int c = (wx * NVW + n) * 32 + ln;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = r0 + mt * 32 + 8 * (q >> 2) + (q & 3);
-            if (r < mg && c < ng) tile[r * WROWS + c] = acc[mt][n][q];
+            for (int q = 0; q < 16; ++q)
+              tile[(r0 + mt * 32 + 8 * (q >> 2) + (q & 3)) * WROWS + c] = acc[mt][n][q];
+            acc[mt][n] = f32x16{};
           }
-          acc[mt][n] = f32x16{};
-        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < LIVE; ++mt)
+#pragma unroll
+          for (int n = 0; n < NVW; ++n) {
+            const int c = (wx * NVW + n) * 32 + ln;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = r0 + mt * 32 + 8 * (q >> 2) + (q & 3);
+              if (r < mg && c < ng) tile[r * WROWS + c] = acc[mt][n][q];
+            }
+            acc[mt][n] = f32x16{};
+          }
+      }
     };
     auto run = [&](auto live) __attribute__((always_inline)) {
       for (int i = 0; i < cnt; ++i) {
