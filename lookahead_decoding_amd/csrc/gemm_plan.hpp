@@ -70,16 +70,18 @@ struct GemmView {
     const size_t stride = tile_elems() / 4;
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < ns; s0 += BATCH) {
+      // every load is issued (a slot past the last re-reads the last one),
+      // so there is no branch around each; only the present slots are added
       float4 t[BATCH];
 #pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        t[j] = s0 + j < ns ? p[(s0 + j) * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < BATCH; ++j) t[j] = p[min(s0 + j, ns - 1) * stride];
 #pragma unroll
       for (int j = 0; j < BATCH; ++j) {
-        y.x += t[j].x;
-        y.y += t[j].y;
-        y.z += t[j].z;
-        y.w += t[j].w;
+        const bool in = s0 + j < ns;
+        y.x += in ? t[j].x : 0.f;
+        y.y += in ? t[j].y : 0.f;
+        y.z += in ? t[j].z : 0.f;
+        y.w += in ? t[j].w : 0.f;
       }
     }
     return y;
