@@ -178,16 +178,22 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
       }
     };
     auto run = [&](auto live) __attribute__((always_inline)) {
+      // (unit, K chunk, row group) of iteration it0 + i, stepped along
+      // rather than divided out every chunk
+      int u = it0 / v.nch;
+      int kc = it0 - u * v.nch;
+      int grp = u % v.groups;
       for (int i = 0; i < cnt; ++i) {
         __syncthreads();
-        const int it = it0 + i;
-        const int u = it / v.nch;
-        const int kc = it - u * v.nch;
-        const int grp = u % v.groups;
         // a wave whose activation tiles all lie past the last row only keeps step
         if (grp * HROWS + wy * MTW * 32 < v.M) {
           compute(i % S, live);
           if (kc == v.nch - 1 || i == cnt - 1) flush(u, live);
+        }
+        if (++kc == v.nch) {
+          kc = 0;
+          ++u;
+          if (++grp == v.groups) grp = 0;
         }
       }
     };
