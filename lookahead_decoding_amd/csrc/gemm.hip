@@ -57,14 +57,14 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned short*>(X), 0, v.M * row_bytes, 0x00020000);
     const int wv = (8 * pw + r8) * row_bytes + ls * 16;
+    // (weight block, row group, K chunk) of the next chunk to issue: chunks
+    // are issued in order, so these step along instead of being divided out
+    int nu = it0 / v.nch;
+    int kc = it0 - nu * v.nch;
+    int wb = nu / v.groups;
+    int grp = nu - wb * v.groups;
     auto issue = [&](int j) __attribute__((always_inline)) {
       unsigned char* dst = smem + (j % S) * BUF;
-      j = min(j, cnt - 1);
-      const int it = it0 + j;
-      const int u = it / v.nch;
-      const int kc = it - u * v.nch;
-      const int wb = u / v.groups;
-      const int grp = u - wb * v.groups;
       const int sw = wb * WROWS * row_bytes + kc * kRB;
 #pragma unroll
       for (int p = 0; p < WP; ++p)
@@ -76,6 +76,14 @@ __device__ __forceinline__ void gemm_body(const GemmView& v, const unsigned shor
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xr, LOPA_LDS(dst + WROWS * kRB + (4 * p + pw) * 1024), 16,
             row * row_bytes + ls * 16, kc * kRB, 0, 0);
+      }
+      // past the range's last chunk, that chunk is loaded again
+      if (j + 1 < cnt && ++kc == v.nch) {
+        kc = 0;
+        if (++grp == v.groups) {
+          grp = 0;
+          ++wb;
+        }
       }
     };
 #pragma unroll
