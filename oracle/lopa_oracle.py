@@ -279,21 +279,45 @@ class HeadOut:
     margin: np.ndarray    # [M] float64: top-1 minus top-2 logit
     logits: np.ndarray | None = None   # [M][V] float64 when asked for
     ent: np.ndarray | None = None      # [M] float64: entropy of softmax(l) / ln V
+    top_tok: np.ndarray | None = None    # [M][T] int64: the T largest logits' tokens
+    top_logit: np.ndarray | None = None  # [M][T] float64: their logits, descending
 
 
-def lmhead_conf(Hrows64: np.ndarray, W, keep_logits: bool = False) -> HeadOut:
+def top_logits(logits: np.ndarray, T: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per row, the T largest logits in descending order and their tokens
+    (the lower token first among equal logits)."""
+    M, V = logits.shape
+    T = min(T, V)
+    tok = np.zeros((M, T), dtype=np.int64)
+    val = np.zeros((M, T))
+    for r in range(M):
+        # every token at or above the T-th largest value (ties at the cut
+        # included), then the order and the cut by (logit desc, token asc)
+        thr = np.partition(logits[r], V - T)[V - T] if T else np.inf
+        cand = np.flatnonzero(logits[r] >= thr)
+        order = sorted(cand.tolist(), key=lambda v: (-logits[r, v], v))[:T]
+        tok[r] = order
+        val[r] = logits[r, order]
+    return tok, val
+
+
+def lmhead_conf(Hrows64: np.ndarray, W, keep_logits: bool = False, top: int = 16) -> HeadOut:
     """Logits l = H_r . W_v for every row r and vocabulary entry v, in
     float64; confidence = max_v softmax(l)_v; token = argmax_v l_v;
     ent = -sum_v p_v ln p_v / ln V, the entropy of the position's
     distribution normalised to [0, 1] (0 when V = 1) -- the H of the
-    alternative branch score of [blog] section 3.2."""
+    alternative branch score of [blog] section 3.2.  ``top``: also the
+    ``top`` largest logits of each row and their tokens (which tokens a
+    near-tied row may validly predict)."""
     W64 = to_f64(W)
     M = Hrows64.shape[0]
     V = W64.shape[0]
     if M == 0:
         e = np.zeros(0)
+        T = min(top, V)
         return HeadOut(e, np.zeros(0, dtype=np.int64), e,
-                       np.zeros((0, V)) if keep_logits else None, e)
+                       np.zeros((0, V)) if keep_logits else None, e,
+                       np.zeros((0, T), dtype=np.int64), np.zeros((0, T)))
     logits = Hrows64 @ W64.T
     P = softmax_rows(logits)
     conf = P.max(axis=1)
@@ -306,7 +330,8 @@ def lmhead_conf(Hrows64: np.ndarray, W, keep_logits: bool = False) -> HeadOut:
     with np.errstate(divide="ignore", invalid="ignore"):
         plogp = np.where(P > 0, P * np.log(P), 0.0)
     ent = -plogp.sum(axis=1) / math.log(V) if V > 1 else np.zeros(M)
-    return HeadOut(conf, arg, margin, logits if keep_logits else None, ent)
+    top_tok, top_val = top_logits(logits, top)
+    return HeadOut(conf, arg, margin, logits if keep_logits else None, ent, top_tok, top_val)
 
 
 # ---------------------------------------------------------------------------
@@ -398,6 +423,8 @@ class StepOut:
     margin_pos: np.ndarray  # [nb_max*B] float64 (inf where not listed)
     sel: Selection
     ent_pos: np.ndarray | None = None   # [nb_max*B] float64 (0 where not listed)
+    top_tok_pos: np.ndarray | None = None    # [nb_max*B][T] int64 (-1 where not listed)
+    top_logit_pos: np.ndarray | None = None  # [nb_max*B][T] float64 (-inf where not listed)
 
 
 def initial_state(inp) -> tuple[np.ndarray, np.ndarray, HeadOut]:
@@ -449,14 +476,21 @@ def verification_step(inp, conf, arg, k: int | None = None,
     arg_pos = np.full(n, -1, dtype=np.int64)
     margin_pos = np.full(n, np.inf)
     ent_pos = np.zeros(n)
+    T = head.top_tok.shape[1] if head.top_tok is not None else 0
+    top_tok_pos = np.full((n, T), -1, dtype=np.int64)
+    top_logit_pos = np.full((n, T), -np.inf)
     for i, r in enumerate(br.rows):
         conf_pos[r] = head.conf[i]
         arg_pos[r] = head.arg[i]
         margin_pos[r] = head.margin[i]
         ent_pos[r] = head.ent[i]
+        if T:
+            top_tok_pos[r] = head.top_tok[i]
+            top_logit_pos[r] = head.top_logit[i]
     if alpha is None:
         sel = branch_select(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos)
     else:
         sel = branch_select_alpha(br.nb, br.br_mask, br.br_tok, conf_pos, arg_pos, ent_pos,
                                   inp.tok, conf, alpha)
-    return StepOut(br, H, head, conf_pos, arg_pos, margin_pos, sel, ent_pos)
+    return StepOut(br, H, head, conf_pos, arg_pos, margin_pos, sel, ent_pos, top_tok_pos,
+                   top_logit_pos)

@@ -43,12 +43,16 @@ class SampleOut:
     conf: np.ndarray     # [M] probability of the drawn token under softmax(l / T)
     arg: np.ndarray      # [M] drawn token
     margin: np.ndarray   # [M] best minus second-best perturbed score
+    top_tok: np.ndarray | None = None     # [M][T] tokens of the T best perturbed scores
+    top_score: np.ndarray | None = None   # [M][T] those scores, descending
 
 
-def lmhead_sample(Hrows64: np.ndarray, W, T: float, seed: int, positions) -> SampleOut:
+def lmhead_sample(Hrows64: np.ndarray, W, T: float, seed: int, positions,
+                  top: int = 16) -> SampleOut:
     """Rows Hrows64 [M][hidden] (float64) at block positions ``positions``
-    [M]; W [V][hidden] (float32 or bf16 bits)."""
-    from .lopa_oracle import to_f64
+    [M]; W [V][hidden] (float32 or bf16 bits).  ``top``: also each row's
+    ``top`` best perturbed scores and their tokens."""
+    from .lopa_oracle import to_f64, top_logits
     W64 = to_f64(W)
     logits = Hrows64 @ W64.T
     V = W64.shape[0]
@@ -56,9 +60,11 @@ def lmhead_sample(Hrows64: np.ndarray, W, T: float, seed: int, positions) -> Sam
     conf = np.zeros(M)
     arg = np.zeros(M, dtype=np.int64)
     margin = np.full(M, math.inf)
+    scores = np.zeros((M, V))
     for r in range(M):
         z = logits[r] / T
         score = z + gumbel(seed, int(positions[r]), V)
+        scores[r] = score
         a = int(np.argmax(score))          # lowest index on a tie
         e = np.exp(z - z.max())
         conf[r] = e[a] / e.sum()
@@ -66,4 +72,5 @@ def lmhead_sample(Hrows64: np.ndarray, W, T: float, seed: int, positions) -> Sam
         if V > 1:
             top2 = np.partition(score, -2)[-2:]
             margin[r] = float(top2[1] - top2[0])
-    return SampleOut(conf, arg, margin)
+    top_tok, top_score = top_logits(scores, top)
+    return SampleOut(conf, arg, margin, top_tok, top_score)

@@ -5,6 +5,10 @@ inputs the oracle sees and compare to the agreement rules:
   bit-exact; a predicted token only where the oracle's top-2 logit margin
   exceeds 1e-2, the winner only where the oracle's best-minus-second branch
   confidence exceeds 1e-3;
+* below those margins the GPU's choice must still be a near-best one: a
+  token whose oracle logit lies within 1e-2 of the row's largest, a winner
+  whose oracle branch confidence lies within 1e-3 of the best (and the
+  GPU's winner is the first maximum of its own branch confidences);
 * confidences within 1e-4 absolute (fp32 workloads) or 2e-2 (bf16);
 * the attention output H within what one bf16 (or fp32) rounding of the
   exact value allows, plus float32 accumulation error.
@@ -55,7 +59,21 @@ def assert_h_close(H_gpu: np.ndarray, H_exact: np.ndarray, dtype: str, what: str
                            f"max err {err.max():.3g}")
 
 
-def assert_head_close(conf_gpu, arg_gpu, conf_ref, arg_ref, margin_ref, dtype, what="head"):
+def assert_near_best_tokens(arg_gpu, top_tok, top_logit, rows_mask, what="head"):
+    """Rows in ``rows_mask`` (near-tied in the oracle): the GPU's token must be
+    one whose oracle logit is within TOK_MARGIN of the row's largest.  The
+    oracle lists each row's largest logits and their tokens; a token outside
+    that list is further than the list's last logit."""
+    for r in np.flatnonzero(rows_mask):
+        t = int(arg_gpu[r])
+        hit = np.flatnonzero(top_tok[r] == t)
+        assert hit.size == 1, f"{what}: row {r} token {t} not among the oracle's largest logits"
+        gap = top_logit[r][0] - top_logit[r][hit[0]]
+        assert gap <= TOK_MARGIN, f"{what}: row {r} token {t} is {gap:.3g} below the best logit"
+
+
+def assert_head_close(conf_gpu, arg_gpu, conf_ref, arg_ref, margin_ref, dtype, what="head",
+                      top_tok=None, top_logit=None):
     conf_gpu = np.asarray(conf_gpu, np.float64)
     err = np.abs(conf_gpu - conf_ref)
     tol = conf_tol(dtype)
@@ -63,7 +81,24 @@ def assert_head_close(conf_gpu, arg_gpu, conf_ref, arg_ref, margin_ref, dtype, w
     sure = margin_ref > TOK_MARGIN
     mism = (np.asarray(arg_gpu) != np.asarray(arg_ref)) & sure
     assert not mism.any(), f"{what}: {mism.sum()} token mismatches among {sure.sum()} sure rows"
+    if top_tok is not None:
+        assert_near_best_tokens(np.asarray(arg_gpu), top_tok, top_logit, ~sure, what)
     return float(err.max()) if err.size else 0.0, int((~sure).sum())
+
+
+def assert_winner_valid(bconf_gpu, w: int, nb: int, bconf_ref, winner_ref: int, margin_ref: float,
+                        margin: float = WIN_MARGIN):
+    """The GPU's winner is the first maximum of its own branch confidences;
+    it equals the oracle's where the oracle's margin exceeds ``margin``, and
+    is otherwise a branch whose oracle confidence is within ``margin`` of the
+    oracle's best."""
+    bc = np.asarray(bconf_gpu)[:nb]
+    assert 0 <= w < nb and bc[w] == bc.max() and np.flatnonzero(bc == bc.max())[0] == w
+    if margin_ref > margin:
+        assert w == winner_ref
+    else:
+        best = float(np.max(bconf_ref[:nb]))
+        assert bconf_ref[w] >= best - margin, (w, bconf_ref[w], best)
 
 
 def gpu_build(dims, k, tau, tok, conf, arg):
@@ -133,13 +168,15 @@ def check_step(inp, conf, arg, ref: O.StepOut, g: dict):
     assert_h_close(g["H"][:nb], H_exact[:nb], cfg.dtype)
     rows = br.rows
     cerr, excl = assert_head_close(g["conf"][rows], g["arg"][rows], ref.conf_pos[rows],
-                                   ref.arg_pos[rows], ref.margin_pos[rows], cfg.dtype)
+                                   ref.arg_pos[rows], ref.margin_pos[rows], cfg.dtype,
+                                   top_tok=ref.top_tok_pos[rows],
+                                   top_logit=ref.top_logit_pos[rows])
     # select
     bc = np.asarray(g["bconf"], np.float64)
     assert np.all(np.abs(bc[:nb] - ref.sel.bconf[:nb]) <= conf_tol(cfg.dtype))
     assert np.all(bc[nb:] == -1)
-    if ref.sel.margin > WIN_MARGIN:
-        assert g["winner"] == ref.sel.winner
+    assert_winner_valid(g["bconf"], g["winner"], nb, ref.sel.bconf, ref.sel.winner,
+                        ref.sel.margin)
     # reuse: the GPU's next state is exactly its own winner's rows
     w = g["winner"]
     np.testing.assert_array_equal(g["tok_next"], g["br_tok"][w])

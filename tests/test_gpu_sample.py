@@ -67,6 +67,10 @@ def test_gpu_lmhead_sample(name, ov, T):
     sure = ref.margin > 1e-3
     assert sure.mean() > 0.9
     np.testing.assert_array_equal(ag[sure], ref.arg[sure])
+    # near-tied draws: the GPU's token has a perturbed score within 1e-3 of the best
+    for i in np.flatnonzero(~sure):
+        hit = np.flatnonzero(ref.top_tok[i] == ag[i])
+        assert hit.size == 1 and ref.top_score[i][0] - ref.top_score[i][hit[0]] <= 1e-3
     np.testing.assert_allclose(cg[sure], ref.conf[sure], rtol=1e-4, atol=1e-7)
 
 

@@ -30,6 +30,26 @@ def test_oracle_head_matches_scipy_softmax():
                                rtol=1e-13)
 
 
+def test_oracle_head_top_logits_by_full_sort():
+    """The T largest logits per row (tokens of equal logits lowest first)
+    against a full lexicographic sort of every row, with planted ties and
+    T reaching V."""
+    rng = np.random.default_rng(7)
+    H = rng.standard_normal((6, 5))
+    W = rng.standard_normal((40, 5)).astype(np.float32)
+    W[[3, 11, 29]] = W[17]          # four tokens share every row's logit
+    for T in (1, 4, 16, 40, 60):
+        out = O.lmhead_conf(H, W, keep_logits=True, top=T)
+        for r in range(H.shape[0]):
+            l = out.logits[r]
+            order = np.lexsort((np.arange(40), -l))[:min(T, 40)]
+            assert out.top_tok[r].tolist() == order.tolist()
+            assert np.array_equal(out.top_logit[r], l[order])
+        assert np.array_equal(out.top_tok[:, 0], out.arg)
+        if T >= 2:
+            np.testing.assert_array_equal(out.top_logit[:, 0] - out.top_logit[:, 1], out.margin)
+
+
 def test_oracle_head_zero_weight_is_uniform():
     H = np.ones((3, 8))
     W = np.zeros((777, 8), np.float32)
