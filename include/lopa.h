@@ -86,8 +86,10 @@ const char* lopa_status_string(int status);
 
 /* Bytes of device workspace that lopa_branch_attn and lopa_lmhead_conf need
  * for these dims (written to *bytes; the larger of the two, so one buffer
- * serves both calls of a step when they are ordered on one stream).  Returns
- * LOPA_OK or LOPA_ERR_INVALID.  Pure host computation. */
+ * serves both calls of a step when they are ordered on one stream).  The
+ * size never decreases as dims->L grows, so a buffer sized for the longest
+ * prefix of a sequence serves every shorter one.  Returns LOPA_OK or
+ * LOPA_ERR_INVALID.  Pure host computation. */
 int lopa_workspace_bytes(const lopa_dims* dims, size_t* bytes);
 
 /*

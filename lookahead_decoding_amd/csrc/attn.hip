@@ -496,6 +496,10 @@ extern "C" int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const voi
   if (need > 0 && (!ws || ws_bytes < need)) return LOPA_ERR_WORKSPACE;
   const int nb_max = dims->k_max + 1;
   if (p.mfma) {
+    // the MFMA kernel addresses K/V through buffer descriptors with 32-bit
+    // byte offsets
+    if (static_cast<long long>(dims->L) * dims->Hkv * dims->d * 2 >= (1LL << 31))
+      return LOPA_ERR_UNSUPPORTED;
     const dim3 grid(p.row_groups, dims->Hkv, p.splits);
     hipLaunchKernelGGL(k_attn_dma, grid, dim3(512), 0, stream, dims->L, dims->B, dims->Hq,
                        dims->Hkv, nb_max, p.splits, nb, static_cast<const unsigned short*>(Kp),

@@ -28,6 +28,29 @@ struct AttnPlan {
   int splits;      // grid.z
 };
 
+// Split count for a prefix of `units` 64-key work units (own blocks
+// included) and wgs workgroups per split.
+inline int attn_splits(int units, int wgs) {
+  int smax = 256 / wgs;
+  if (smax > units / 2) smax = units / 2;
+  if (smax > kAttnMaxSplits) smax = kAttnMaxSplits;
+  int splits = 1;
+  int best = units;
+  for (int s = 2; s <= smax; ++s) {
+    const int t = (units + s - 1) / s + kAttnSplitCostUnits;
+    if (t < best) {
+      best = t;
+      splits = s;
+    }
+  }
+  return splits;
+}
+
+inline int attn_units(const lopa_dims& d) {
+  return (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock +
+         (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
+}
+
 inline AttnPlan attn_plan(const lopa_dims& d) {
   AttnPlan p{};
   p.mfma = d.dtype == LOPA_BF16 && d.d == 128;
@@ -35,31 +58,31 @@ inline AttnPlan attn_plan(const lopa_dims& d) {
   if (!p.mfma) return p;
   const int rows = (d.k_max + 1) * d.B * (d.Hq / d.Hkv);
   p.row_groups = (rows + kAttnRowsPerWG - 1) / kAttnRowsPerWG;
-  const int wgs = p.row_groups * d.Hkv;
-  const int units = (d.L + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock +
-                    (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
-  int smax = 256 / wgs;
-  if (smax > units / 2) smax = units / 2;
-  if (smax > kAttnMaxSplits) smax = kAttnMaxSplits;
-  p.splits = 1;
-  int best = units;
-  for (int s = 2; s <= smax; ++s) {
-    const int t = (units + s - 1) / s + kAttnSplitCostUnits;
-    if (t < best) {
-      best = t;
-      p.splits = s;
-    }
-  }
+  p.splits = attn_splits(attn_units(d), p.row_groups * d.Hkv);
   return p;
 }
 
 // Partials of the split prefix: per split, KV head and query row, the
-// unnormalised output (d floats), the running max and the running sum.
+// unnormalised output (d floats), the running max and the running sum.  The
+// split count is not monotone in the prefix length, so the size returned is
+// the largest over every prefix up to d.L: a buffer sized for a prefix also
+// serves every shorter one (a sequence decoded block after block grows its
+// prefix and keeps one workspace).
 inline size_t attn_workspace_bytes(const lopa_dims& d) {
   const AttnPlan p = attn_plan(d);
-  if (p.splits <= 1) return 0;
+  if (!p.mfma) return 0;
+  const int wgs = p.row_groups * d.Hkv;
+  const int u0 = (d.B + kAttnKeysPerBlock - 1) / kAttnKeysPerBlock;
+  int cap = 256 / wgs;
+  cap = cap < kAttnMaxSplits ? cap : kAttnMaxSplits;
+  int smax = 1;
+  for (int u = u0; u <= attn_units(d) && smax < cap; ++u) {
+    const int s = attn_splits(u, wgs);
+    smax = s > smax ? s : smax;
+  }
+  if (smax <= 1) return 0;
   const size_t rows = static_cast<size_t>(d.k_max + 1) * d.B * (d.Hq / d.Hkv);
-  return static_cast<size_t>(p.splits) * d.Hkv * rows * (d.d + 2) * 4u;
+  return static_cast<size_t>(smax) * d.Hkv * rows * (d.d + 2) * 4u;
 }
 
 }  // namespace lopa

@@ -296,6 +296,9 @@ static int check_model(const lopa_dims* d, const lopa_model_dims* md) {
   if (gm.qkv.units > lopa::kSlotTableMax || gm.o.units > lopa::kSlotTableMax ||
       gm.gu.units > lopa::kSlotTableMax || gm.down.units > lopa::kSlotTableMax)
     return LOPA_ERR_UNSUPPORTED;
+  // the consumers' slot table holds one byte per unit
+  if (gm.qkv.smax > 255 || gm.o.smax > 255 || gm.gu.smax > 255 || gm.down.smax > 255)
+    return LOPA_ERR_UNSUPPORTED;
   return LOPA_OK;
 }
 
