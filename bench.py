@@ -269,24 +269,34 @@ def cpu_baseline(inp, conf, arg, seconds: float) -> dict:
                       f"select) in {el:.1f} s; cores = BLAS threads of the fp64 matmul"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the verification step "
-              "runs on a single GPU and is not sharded across GPUs.", file=sys.stderr)
-        sys.exit(2)
+PAGES_CONTEXT = {
+    "note": "the pages' own figures, on trained D2F weights and real benchmarks (other "
+            "hardware); not comparable to a single synthetic verification step",
+    "tpf_d2f_dream_gsm8k": [3.1, 10.1],
+    "tpf_d2f_diffucoder_humanevalplus": [2.8, 8.3],
+    "tokens_per_s_lopa_dist_ascend910c_mbpp": 1073.9,
+    "tokens_per_s_lopa_dist_ascend910c_gsm8k": 856.5,
+    "extra_branch_compute_overhead": "10-15%",
+}
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measure_workload(name: str, args, headline: bool) -> tuple[dict, dict]:
+    """Time the four-call step on one workload.  Returns the per-workload
+    record and the context the headline extras need."""
     import torch
 
     import lookahead_decoding_amd as lopa
     import synth
     from lookahead_decoding_amd.step import StepBuffers, dims_of, initial_pass, run_step, to_device
 
-    name = args.workload or synth.HEADLINE
+    progress(f"workload {name}: drawing inputs")
     inp = synth.make_inputs(name)
     cfg = inp.cfg
     dims = dims_of(cfg)
-    torch.cuda.set_device(0)
-    lopa.lib()
     stream = torch.cuda.current_stream()
     x = {k: to_device(v) for k, v in inp.arrays().items()}
     buf = StepBuffers(dims)
@@ -294,15 +304,16 @@ def main():
     x["conf"], x["arg"] = conf0, arg0
     torch.cuda.synchronize()
 
-    # one step to learn nb and M (state is fixed, so every step is identical)
-    run_step(dims, cfg.k, cfg.tau, x, buf)
-    torch.cuda.synchronize()
-    nb = int(buf.nb.item())
-    M = int(buf.row_ptr[nb].item())
-    alg = algorithmic(cfg, nb, M)
+    def learn(k):
+        # one step to learn nb and M (the state is fixed, so every step is identical)
+        run_step(dims, k, cfg.tau, x, buf)
+        torch.cuda.synchronize()
+        nb = int(buf.nb.item())
+        return nb, int(buf.row_ptr[nb].item())
 
-    def step():
-        run_step(dims, cfg.k, cfg.tau, x, buf)
+    nb0, M0 = learn(0) if cfg.k > 0 else (None, None)
+    nb, M = learn(cfg.k)
+    alg = algorithmic(cfg, nb, M)
 
     graph = None
     if args.graph:
@@ -310,68 +321,66 @@ def main():
         s = torch.cuda.Stream()
         s.wait_stream(stream)
         with torch.cuda.stream(s):
-            step()
+            run_step(dims, cfg.k, cfg.tau, x, buf)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=s):
-            step()
+            run_step(dims, cfg.k, cfg.tau, x, buf)
         torch.cuda.synchronize()
 
     # Eager: every SAMPLE-th step of the timed loop carries HIP events around
     # its LM-head call (the roofline's duration, taken inside the timed
     # region); the other steps carry none.  Event records between kernels
     # hold the stream up: three per step cost 6 us a step (4340 against 4460
-    # steps/s at prefix 512, batch 32, k 4).
+    # steps/s at prefix 512, batch 32, k 4).  The k = 0 leg (the anchor
+    # alone, for the cost of the extra branches) runs the same loop.
     SAMPLE = 10
-    head_ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for i in range(0, args.steps, SAMPLE)}
 
-    def timed_step(i):
-        ev_i = head_ev.get(i)
-        lopa.lopa_branch_build(dims, cfg.k, cfg.tau, x["tok"], x["conf"], x["arg"], buf.nb,
-                               buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr)
-        lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb, buf.H,
-                              buf.ws)
-        if ev_i:
-            ev_i[0].record(stream)
-        lopa.lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
-                              buf.arg, None, buf.ws)
-        if ev_i:
-            ev_i[1].record(stream)
-        lopa.lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg,
-                                buf.bconf, buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
+    def timed_loop(k):
+        head_ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for i in range(0, args.steps, SAMPLE)}
 
-    for _ in range(args.warmup):
-        graph.replay() if graph else step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graph.replay() if graph else timed_step(i)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms = el / args.steps * 1e3
-    head_timed_us = None if graph else \
-        float(np.mean([a.elapsed_time(b) for a, b in head_ev.values()])) * 1e3
+        def timed_step(i):
+            ev_i = head_ev.get(i)
+            lopa.lopa_branch_build(dims, k, cfg.tau, x["tok"], x["conf"], x["arg"], buf.nb,
+                                   buf.br_tok, buf.br_mask, buf.rows, buf.row_ptr)
+            lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], buf.nb,
+                                  buf.H, buf.ws)
+            if ev_i:
+                ev_i[0].record(stream)
+            lopa.lopa_lmhead_conf(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
+                                  buf.arg, None, buf.ws)
+            if ev_i:
+                ev_i[1].record(stream)
+            lopa.lopa_branch_select(dims, buf.nb, buf.br_mask, buf.br_tok, buf.conf, buf.arg,
+                                    buf.bconf, buf.winner, buf.tok_next, buf.conf_next,
+                                    buf.arg_next)
+
+        use_graph = graph is not None and k == cfg.k
+        for i in range(args.warmup):
+            graph.replay() if use_graph else timed_step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graph.replay() if use_graph else timed_step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        head_us = None if use_graph else \
+            float(np.mean([a.elapsed_time(b) for a, b in head_ev.values()])) * 1e3
+        return ms, head_us
+
+    progress(f"workload {name}: timing {args.steps} steps")
+    ms, head_timed_us = timed_loop(cfg.k)
+    ms0, head0_us = timed_loop(0) if cfg.k > 0 else (None, None)
+
     # the distribution of step times, from a second pass of the same steps
     # with an event at every step boundary (outside the timed region)
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     step_ev[0].record(stream)
     for i in range(args.steps):
-        graph.replay() if graph else step()
+        graph.replay() if graph else run_step(dims, cfg.k, cfg.tau, x, buf)
         step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     step_us = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]) * 1e3
-
-    # the same step with no lookahead branch (k = 0: the anchor alone), for the
-    # cost of the extra branches
-    k0_us = None
-    if cfg.k > 0 and not graph:
-        for i in range(args.warmup + 50):
-            if i == args.warmup:
-                torch.cuda.synchronize()
-                t1 = time.perf_counter()
-            run_step(dims, 0, cfg.tau, x, buf)
-        torch.cuda.synchronize()
-        k0_us = (time.perf_counter() - t1) / 50 * 1e6
 
     # Per-call durations with HIP events on the stream the calls run on.
     K = max(20, min(args.steps, 100))
@@ -394,50 +403,39 @@ def main():
     torch.cuda.synchronize()
     per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)])
     call_us = per.mean(axis=0) * 1e3
-    # the entropy-carrying LM head and the alternative select on the same rows
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for i in range(K):
-        e = ev2[i]
-        e[0].record(stream)
-        lopa.lopa_lmhead_conf_ent(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb, buf.conf,
-                                  buf.arg, buf.ent, None, buf.ws)
-        e[1].record(stream)
-        lopa.lopa_branch_select_alpha(dims, 0.5, x["tok"], x["conf"], buf.nb, buf.br_mask,
-                                      buf.br_tok, buf.conf, buf.arg, buf.ent, buf.bconf,
-                                      buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
-        e[2].record(stream)
-        lopa.lopa_lmhead_sample(dims, 0.9, 1000 + i, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb,
-                                buf.conf, buf.arg, None, buf.ws)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    alt_us = np.array([[ev2[i][j].elapsed_time(ev2[i][j + 1]) for j in range(3)]
-                       for i in range(K)]).mean(axis=0) * 1e3
+    calls = {"branch_build": round(float(call_us[0]), 2),
+             "branch_attn": round(float(call_us[1]), 2),
+             "lmhead_conf": round(float(call_us[2]), 2),
+             "branch_select": round(float(call_us[3]), 2)}
+    if headline:
+        # the entropy-carrying LM head and the alternative select on the same rows
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for i in range(K):
+            e = ev2[i]
+            e[0].record(stream)
+            lopa.lopa_lmhead_conf_ent(dims, buf.H, x["W"], buf.rows, buf.row_ptr, buf.nb,
+                                      buf.conf, buf.arg, buf.ent, None, buf.ws)
+            e[1].record(stream)
+            lopa.lopa_branch_select_alpha(dims, 0.5, x["tok"], x["conf"], buf.nb, buf.br_mask,
+                                          buf.br_tok, buf.conf, buf.arg, buf.ent, buf.bconf,
+                                          buf.winner, buf.tok_next, buf.conf_next, buf.arg_next)
+            e[2].record(stream)
+            lopa.lopa_lmhead_sample(dims, 0.9, 1000 + i, buf.H, x["W"], buf.rows, buf.row_ptr,
+                                    buf.nb, buf.conf, buf.arg, None, buf.ws)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        alt_us = np.array([[ev2[i][j].elapsed_time(ev2[i][j + 1]) for j in range(3)]
+                           for i in range(K)]).mean(axis=0) * 1e3
+        calls.update({"lmhead_conf_ent": round(float(alt_us[0]), 2),
+                      "branch_select_alpha": round(float(alt_us[1]), 2),
+                      "lmhead_sample": round(float(alt_us[2]), 2)})
     # the roofline uses the LM-head call timed inside the timed loop (eager), else the
     # separate per-call loop (graph replay has no per-call events)
     head_us = head_timed_us if head_timed_us is not None else float(call_us[2])
-    tr = HEAD_TRAFFIC.get(cfg.name)
-    traffic = tr[1] if tr is not None and tr[0] == head_source_hash() else None
-    achieved = alg["head_bytes"] / (head_us * 1e-6) / 1e9
-    head_tflops = alg["head_flops"] / (head_us * 1e-6) / 1e12
-    # the LM head's bound: the roof whose time at peak is the longer (rows above
-    # ~315 per call pass the bf16 ridge and make it MFMA-bound)
-    mfma_bound = (alg["head_flops"] / (BF16_PEAK_TFLOPS * 1e12) >
-                  alg["head_bytes"] / (HBM_PEAK_GBS * 1e9))
-
     steps_s = 1e3 / ms
-    out = {
-        "metric": "LoPA verification steps/s (7B shapes, 1 GPU)",
-        "value": round(steps_s, 2),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    rec = {
+        "steps_per_s": round(steps_s, 2),
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; random Q/K/V and LM-head weight of 7B shape)",
         "config": {"workload": cfg.name, "L": cfg.L, "B": cfg.B, "masked": cfg.m, "k": cfg.k,
                    "branches": nb, "lmhead_rows": M, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "hidden": cfg.hidden, "V": cfg.V, "tau": cfg.tau,
@@ -452,32 +450,93 @@ def main():
                                         (alg["head_flops"] + alg["attn_flops"]) /
                                         (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
         "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
-        "step_us_k0": None if k0_us is None else round(k0_us, 2),
-        "t_k_over_t_k0": None if k0_us is None else round(ms * 1e3 / k0_us, 4),
-        "call_us": {"branch_build": round(float(call_us[0]), 2),
-                    "branch_attn": round(float(call_us[1]), 2),
-                    "lmhead_conf": round(float(call_us[2]), 2),
-                    "branch_select": round(float(call_us[3]), 2),
-                    "lmhead_conf_ent": round(float(alt_us[0]), 2),
-                    "branch_select_alpha": round(float(alt_us[1]), 2),
-                    "lmhead_sample": round(float(alt_us[2]), 2)},
-        "roofline": ({"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
-                      "bound": "mfma", "achieved": round(head_tflops, 1),
-                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": round(head_tflops / BF16_PEAK_TFLOPS, 4),
-                      "traffic": traffic,
-                      "algorithmic_flops_per_call": alg["head_flops"],
-                      "algorithmic_bytes_per_call": alg["head_bytes"],
-                      "call_us": round(head_us, 2),
-                      "hbm_gbs": round(achieved, 1)} if mfma_bound else
-                     {"kernel": "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)",
-                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                      "traffic": traffic,
-                      "algorithmic_bytes_per_call": alg["head_bytes"],
-                      "call_us": round(head_us, 2),
-                      "mfma_tflops": round(head_tflops, 1)}),
+        "k0": None if ms0 is None else {"branches": nb0, "lmhead_rows": M0,
+                                        "ms_per_step": round(ms0, 4),
+                                        "lmhead_us": None if head0_us is None
+                                        else round(head0_us, 2)},
+        "t_k_over_t_k0": None if ms0 is None else round(ms / ms0, 4),
+        "call_us": calls,
+        "roofline": head_roofline(cfg, alg, head_us),
+        "attn_roofline": attn_roofline(alg, float(call_us[1])),
     }
+    ctx = dict(inp=inp, cfg=cfg, dims=dims, x=x, buf=buf)
+    return rec, ctx
+
+
+def head_roofline(cfg, alg, head_us: float) -> dict:
+    """LM-head call: algorithmic bytes (or flops, past the bf16 ridge) per
+    call / its event-timed duration, against the MI355X peak of that roof."""
+    tr = HEAD_TRAFFIC.get(cfg.name)
+    traffic = tr[1] if tr is not None and tr[0] == head_source_hash() else None
+    achieved = alg["head_bytes"] / (head_us * 1e-6) / 1e9
+    tflops = alg["head_flops"] / (head_us * 1e-6) / 1e12
+    # the roof whose time at peak is the longer (rows above ~315 per call
+    # pass the bf16 ridge and make it MFMA-bound)
+    mfma_bound = (alg["head_flops"] / (BF16_PEAK_TFLOPS * 1e12) >
+                  alg["head_bytes"] / (HBM_PEAK_GBS * 1e9))
+    kern = "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)"
+    if mfma_bound:
+        return {"kernel": kern, "bound": "mfma", "achieved": round(tflops, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_call": alg["head_flops"],
+                "algorithmic_bytes_per_call": alg["head_bytes"], "call_us": round(head_us, 2),
+                "hbm_gbs": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+    return {"kernel": kern, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "algorithmic_bytes_per_call": alg["head_bytes"],
+            "call_us": round(head_us, 2), "mfma_tflops": round(tflops, 1),
+            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def attn_roofline(alg, attn_us: float) -> dict:
+    """Attention call (event-timed, so it includes one event gap of a few
+    microseconds): its flops against the bf16 MFMA peak and its algorithmic
+    bytes against HBM."""
+    tflops = alg["attn_flops"] / (attn_us * 1e-6) / 1e12
+    gbs = alg["attn_bytes"] / (attn_us * 1e-6) / 1e9
+    return {"call_us": round(attn_us, 2), "tflops": round(tflops, 1),
+            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_flops_per_call": alg["attn_flops"],
+            "algorithmic_bytes_per_call": alg["attn_bytes"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the verification step "
+              "runs on a single GPU and is not sharded across GPUs.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lookahead_decoding_amd as lopa
+    import synth
+
+    torch.cuda.set_device(0)
+    lopa.lib()
+    head_name = args.workload or synth.HEADLINE
+    rec, ctx = measure_workload(head_name, args, headline=True)
+    inp, cfg, dims, x = ctx["inp"], ctx["cfg"], ctx["dims"], ctx["x"]
+    out = {
+        "metric": "LoPA verification steps/s (7B shapes, 1 GPU)",
+        "value": rec["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random Q/K/V and LM-head weight of 7B shape)",
+        "config": rec["config"],
+    }
+    for key in ("branch_tokens_per_s", "lmhead_rows_per_s", "step_hbm_frac", "step_mfma_frac",
+                "step_roofline_frac", "step_us_p10_p50_p90", "k0", "t_k_over_t_k0", "call_us",
+                "roofline", "attn_roofline"):
+        out[key] = rec[key]
     if args.copy_probe:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         b = torch.empty_like(a)
@@ -486,6 +545,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_probe_bytes"] = a.numel() * a.element_size()
     if not args.no_decode:
+        progress("block decoding")
         seed = 0x10FA + inp.seed
         out["decode"] = {
             "data": "token-keyed synthetic Q/K/V (Philox4x32-10, Irwin-Hall N(0,1)) and "
@@ -499,11 +559,37 @@ def main():
                                                      temperature=0.9),
         }
     if not args.no_model and cfg.dtype == "bf16":
+        progress("28-layer model step")
         out["model_step"] = model_measure(cfg, inp, args.model_steps, 5)
+    del ctx, x
+    torch.cuda.empty_cache()
+    # every 7B workload, each timed like the headline (its own inputs)
+    names = [] if args.workload else list(synth.SEVEN_B)
+    others = {}
+    cpu_inputs = {head_name: inp}
+    for name in names:
+        if name == head_name:
+            others[name] = {k: v for k, v in rec.items()}
+            continue
+        r, c = measure_workload(name, args, headline=False)
+        others[name] = r
+        cpu_inputs[name] = c["inp"]
+        del c
+        torch.cuda.empty_cache()
+    if others:
+        out["workloads"] = others
+    out["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         import oracle as O  # noqa: F401  (CPU baseline leg only)
         c, a, _ = O.initial_state(inp)
         out["cpu_baseline"] = cpu_baseline(inp, c, a, args.cpu_seconds)
+        # one bounded oracle step of every other workload
+        for name, winp in cpu_inputs.items():
+            if name == head_name or name not in others:
+                continue
+            c, a, _ = O.initial_state(winp)
+            others[name]["cpu_baseline"] = cpu_baseline(winp, c, a, 0.0)
     print(json.dumps(out), flush=True)
 
 
