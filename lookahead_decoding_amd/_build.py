@@ -39,6 +39,10 @@ def _run(cmd: list[str]) -> None:
         sys.stderr.write(err + "\n")
 
 
+# Per-source extra flags (none at present).
+EXTRA: dict[str, list[str]] = {}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
@@ -46,7 +50,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

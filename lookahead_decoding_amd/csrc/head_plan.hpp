@@ -69,6 +69,57 @@ __host__ __device__ inline HeadGroups head_groups(int M) {
   return HeadGroups{wide, g, 8 * (kHeadParts / 8 / g), (tiles + g - 1) / g};
 }
 
+// The wide kernel (k_lmhead_wide): four waves, one per SIMD, each of them
+// both loading and computing, with large register tiles.  Its row groups
+// hold at most kWideMaxTiles 32-row tiles (the LDS ring holds every row of a
+// group); th = 4q + r tiles per group: each wave owns q tiles against every
+// weight tile of a pass, and the r remaining tiles are shared out by weight
+// tile (wave w takes weight tiles w, w + 4, ...), so every wave runs the
+// same number of MFMAs.  tw: weight tiles per pass (8 while the LDS allows
+// it, else 4).  It serves the row-tile counts where it measured faster than
+// the narrow kernel (k_lmhead_mfma) in a same-box comparison at every count
+// from 5 to 32 tiles at the 7B shapes: 5, 6, 9, 13, 17 and 18 tiles (by 12,
+// 3, 8, 2, 4 and 2 %); the narrow kernel serves every other count.
+constexpr int kHeadNarrowRows = 128;
+constexpr int kWideMaxTiles = 13;
+
+struct WideGroups {
+  int tw, th, groups, nparts;
+};
+
+__host__ __device__ inline WideGroups wide_groups(int M) {
+  const int tiles = (M + 31) / 32;
+  const int g = (tiles + kWideMaxTiles - 1) / kWideMaxTiles;
+  const int th = (tiles + g - 1) / g;
+  return WideGroups{th <= 7 ? 8 : 4, th, g, 8 * (kHeadParts / 8 / g)};
+}
+
+__host__ __device__ inline bool wide_takes(int M) {
+  const int t = (M + 31) / 32;
+  return t == 5 || t == 6 || t == 9 || t == 13 || t == 17 || t == 18;
+}
+
+// Vocabulary parts per row of whichever MFMA kernel serves M rows (wide:
+// whether the wide kernel was launched beside the narrow one).
+__host__ __device__ inline int head_nparts(int M, bool wide) {
+  return wide && wide_takes(M) ? wide_groups(M).nparts : head_groups(M).nparts;
+}
+
+// Largest byte range of W one MFMA workgroup addresses: the rows of the
+// widest vocabulary part over every row count the device may see (up to
+// m_max) plus one pass of 256 rows read past its end.
+inline long long head_part_bytes_max(const lopa_dims& d) {
+  const HeadPlan p = head_plan(d);
+  int nparts = kHeadParts;
+  for (int m = 1; m <= p.m_max; m += 32) {
+    const int n = head_nparts(m, true);
+    nparts = n < nparts ? n : nparts;
+  }
+  const long long t16 = (d.V + 15) / 16;
+  const long long rows = (t16 + nparts - 1) / nparts * 16 + 256;
+  return rows * d.Hq * d.d * 2;
+}
+
 // Per (row, vocabulary tile) partial: max logit (float), scaled sum (float),
 // argmax or sample (int32), entropy term or perturbed best score (float),
 // scaled logit of the sample (float) -- five planes of m_max * ntiles.

@@ -72,16 +72,17 @@ __device__ __forceinline__ float gumbel(unsigned x) {
 // Sampling partial of one lane's logits for one LM-head row at block
 // position pos (layout as row_partial below), merged with the other lane
 // half that holds the same row.
-template <int NV>
+template <int NV, int VS = 32, int NL = NV>
 __device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], int vb, int h,
                                                        int vend, const Sampling& smp,
                                                        unsigned pos) {
+  static_assert(NL <= NV, "tiles");
   SPartial p = empty_spartial();
 #pragma unroll
-  for (int n = 0; n < NV; ++n)
+  for (int n = 0; n < NL; ++n)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int v0 = vb + n * 32 + 8 * q4 + 4 * h;   // a multiple of 4
+      const int v0 = vb + n * VS + 8 * q4 + 4 * h;   // a multiple of 4
       unsigned key0 = smp.k0, key1 = smp.k1;
       // the key schedule in vector registers: hoisted into scalar registers
       // for every call at once, it spills
@@ -107,10 +108,10 @@ __device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], in
   if (p.i != 0x7fffffff) {
     float s = 0.f;
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
+    for (int n = 0; n < NL; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = vb + n * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int v = vb + n * VS + 8 * (r >> 2) + 4 * h + (r & 3);
         if (v < vend) s += exp2f((a[n][r] * smp.inv_t - p.m) * kLog2e);
       }
     p.s = s;
@@ -119,9 +120,10 @@ __device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], in
 }
 
 // Online-softmax partial of one lane's logits for one LM-head row:
-// a[n][r] = logit of vocabulary entry vb + 32n + 8(r/4) + 4h + r%4 (the
-// 32x32 MFMA output layout, h = lane / 32), merged with the other lane half
-// that holds the same row.  ENT: also the entropy term t (else t = 0).
+// a[n][r] = logit of vocabulary entry vb + VS n + 8(r/4) + 4h + r%4 (the
+// 32x32 MFMA output layout, h = lane / 32; VS = 32 for adjacent weight
+// tiles), merged with the other lane half that holds the same row.  ENT:
+// also the entropy term t (else t = 0).
 //
 // Straight-line code: the max and its index move together by selects when
 // an entry is strictly larger (the entries ascend in this order, so the
@@ -131,15 +133,16 @@ __device__ __forceinline__ SPartial row_partial_sample(const f32x16 (&a)[NV], in
 // (l - max) log2 e is <= 0, and a term below 2^-126, which the hardware
 // flushes to zero, is far below half an ulp of a sum that holds the max's
 // own term 1.
-template <int NV, bool ENT, bool MASKED>
+template <int NV, bool ENT, bool MASKED, int VS = 32, int NL = NV>
 __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, int h, int vend) {
+  static_assert(NL <= NV, "tiles");
   Partial p = empty_partial();
   const int v0 = vb + 4 * h;
 #pragma unroll
-  for (int n = 0; n < NV; ++n)
+  for (int n = 0; n < NL; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int v = v0 + n * 32 + 8 * (r >> 2) + (r & 3);
+      const int v = v0 + n * VS + 8 * (r >> 2) + (r & 3);
       const bool c = MASKED ? (v < vend) & (a[n][r] > p.m) : a[n][r] > p.m;
       p.m = c ? a[n][r] : p.m;
       p.i = c ? v : p.i;
@@ -147,13 +150,13 @@ __device__ __forceinline__ Partial row_partial(const f32x16 (&a)[NV], int vb, in
   if (!MASKED || p.i != 0x7fffffff) {
     float s = 0.f, t = 0.f;
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
+    for (int n = 0; n < NL; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float dl = a[n][r] - p.m;
         const float e = __builtin_amdgcn_exp2f(dl * kLog2e);
         if constexpr (MASKED) {
-          const bool ok = v0 + n * 32 + 8 * (r >> 2) + (r & 3) < vend;
+          const bool ok = v0 + n * VS + 8 * (r >> 2) + (r & 3) < vend;
           s += ok ? e : 0.f;
           if constexpr (ENT) t = ok ? fmaf(e, dl, t) : t;
         } else {
@@ -478,9 +481,11 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
 // the second reader is served from that XCD's L2 (or the MALL behind it).
 // MODE: conf only, + entropy term, or temperature sampling (ws_t then
 // holds the perturbed best score, ws_z the scaled logit of the sample).
+// wide: the wide kernel is launched beside this one and serves the row
+// counts wide_takes() names.
 template <int MODE>
 __global__ void __launch_bounds__(kHeadThreads)
-k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
+k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
               const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
@@ -488,7 +493,7 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
               float* __restrict__ ws_z, const Sampling smp, float* __restrict__ logits_out) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHeadSmem];
   const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
-  if (M <= 0) return;
+  if (M <= 0 || (wide && wide_takes(M))) return;
   const HeadGroups g = head_groups(M);
   const int b = blockIdx.x;
   const int q = b >> 3;
@@ -506,6 +511,541 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int h_bytes,
     else head_body<4, 2, 2, MODE>(LOPA_ARGS);
   } else {
     head_body<2, 2, 2, MODE>(LOPA_ARGS);
+  }
+#undef LOPA_ARGS
+}
+
+// ---------------------------------------------------------------------------
+// Wide MFMA kernel (the row counts wide_takes() names)
+// ---------------------------------------------------------------------------
+//
+// Four waves (one per SIMD, up to 512 registers each) hold large register
+// tiles: wave w owns q activation tiles against all tw weight tiles of a
+// pass (q tw MFMAs per 16-wide K step from tw + q fragments), plus its share
+// of the r remaining activation tiles (their pairs with weight tiles w,
+// w + 4, ...): at 13 tiles every wave runs 13 MFMAs per step from 9
+// fragments, where the narrow kernel's 2 x 2 tiles read 4 fragments for 4.
+// The accumulators live in the matrix (AGPR) registers.  Every wave also
+// issues its share of the loads that fill the LDS rings (the weight: three
+// stages, two chunks in flight; the group's activation rows: two stages, one
+// chunk in flight, from L2), so no wave is spent on loading alone.  One
+// barrier per K chunk, taken in K step 2: fragments are read two steps
+// ahead, so by then the chunk's stages hold nothing still to be read, and
+// the two steps after it read the next chunk while their MFMAs run.  The
+// barrier waits for this wave's own loads of the next chunk (vmcnt) and its
+// LDS reads (lgkmcnt), and neither it nor the compiler lets memory accesses
+// move across it (a __syncthreads() would wait for every load in flight).
+//
+// Measured against the narrow kernel (same box, 7B shapes): faster where
+// the narrow kernel changes layout (5, 6, 9, 17, 18 tiles) and by 2 % at 13,
+// slower elsewhere.  Alone, its MFMA work with the LDS fragment reads takes
+// 327 us at 13 tiles (1.38 PFLOP/s; back-to-back MFMA peaks at 2.0 PFLOP/s on
+// this part) and its loads with the reads 240-280 us, but together 495 us:
+// the LDS writes of the loads and the fragment reads compete, and the sum
+// moves about 50-65 bytes per clock through each CU's LDS in both kernels.
+
+// Entry r of a lane's 16 (the 32x32 MFMA output layout) lies at vocabulary
+// vb + 4h + kTileOff(r).  The folds below compare these compile-time offsets
+// against one per-lane limit and keep the winning entry's r, so no per-entry
+// index is ever held in a register.
+__device__ __forceinline__ constexpr int kTileOff(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Online fold of one 32x32 output tile into a lane's running partial: the
+// lane holds 16 logits of its row.  A lane folds its entries in ascending
+// vocabulary order, so a strictly larger value is needed to move the argmax
+// (the lowest index keeps a tie).  Only 16 values are live at a time.  The
+// two lane halves of a row are merged once, after the last fold.
+template <bool ENT, bool MASKED>
+__device__ __forceinline__ void fold_tile(Partial& p, const f32x16& a, int vb, int h, int vend) {
+  const int lim = vend - vb - 4 * h;   // entries with kTileOff(r) < lim are live
+  float m = -INFINITY;
+  int ri = -1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const bool c = MASKED ? (kTileOff(r) < lim) & (a[r] > m) : a[r] > m;
+    m = c ? a[r] : m;
+    ri = c ? r : ri;
+  }
+  if (MASKED && ri < 0) return;   // no live entry in this tile
+  const int i = vb + 4 * h + 8 * (ri >> 2) + (ri & 3);
+  const bool take = m > p.m;
+  const float M = take ? m : p.m;
+  p.i = take ? i : p.i;
+  // the running sums rescaled to the new maximum (none yet: s = 0)
+  const float d = p.s > 0.f ? p.m - M : 0.f;
+  const float cs = p.s > 0.f ? __builtin_amdgcn_exp2f(d * kLog2e) : 0.f;
+  float s = 0.f, t = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float dl = a[r] - M;
+    const float e = __builtin_amdgcn_exp2f(dl * kLog2e);
+    if constexpr (MASKED) {
+      const bool ok = kTileOff(r) < lim;
+      s += ok ? e : 0.f;
+      if constexpr (ENT) t = ok ? fmaf(e, dl, t) : t;
+    } else {
+      s += e;
+      if constexpr (ENT) t = fmaf(e, dl, t);
+    }
+  }
+  if constexpr (ENT) p.t = fmaf(cs, fmaf(d, p.s, p.t), t);
+  p.s = fmaf(cs, p.s, s);
+  p.m = M;
+}
+
+// The same for temperature sampling: (max, sum) over z = l / T and the best
+// perturbed score z + G with its index and z.  Noise of entry v: word v % 4
+// of Philox4x32-10 at counter (v / 4, pos, kSampleTag, 0).
+__device__ __forceinline__ void fold_tile_sample(SPartial& p, const f32x16& a, int vb, int h,
+                                                 int vend, const Sampling& smp, unsigned pos) {
+  const int lim = vend - vb - 4 * h;
+  const unsigned q0 = static_cast<unsigned>(vb + 4 * h) >> 2;   // vb + 4h is a multiple of 4
+  float m = -INFINITY;
+  int ri = -1;
+  float g = p.g, zb = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    unsigned key0 = smp.k0, key1 = smp.k1;
+    __asm__ volatile("" : "+v"(key0), "+v"(key1));
+    const U32x4 wd = philox4x32_10(U32x4{q0 + 2u * q4, pos, kSampleTag, 0u}, key0, key1);
+    const unsigned xs[4] = {wd.x0, wd.x1, wd.x2, wd.x3};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * q4 + j;
+      const bool live = kTileOff(r) < lim;
+      const float z = a[r] * smp.inv_t;
+      m = live ? fmaxf(m, z) : m;
+      const float gv = z + gumbel(xs[j]);
+      const bool c = live & (gv > g);
+      g = c ? gv : g;
+      zb = c ? z : zb;
+      ri = c ? r : ri;
+    }
+  }
+  if (m == -INFINITY) return;
+  if (ri >= 0) {
+    p.g = g;
+    p.z = zb;
+    p.i = vb + 4 * h + 8 * (ri >> 2) + (ri & 3);
+  }
+  const float M = fmaxf(m, p.m);
+  const float cs = p.s > 0.f ? __builtin_amdgcn_exp2f((p.m - M) * kLog2e) : 0.f;
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e = __builtin_amdgcn_exp2f((a[r] * smp.inv_t - M) * kLog2e);
+    s += kTileOff(r) < lim ? e : 0.f;
+  }
+  p.s = fmaf(cs, p.s, s);
+  p.m = M;
+}
+
+template <int MODE, bool MASKED, typename RP>
+__device__ __forceinline__ void fold_tile_mode(RP& p, const f32x16& a, int vb, int h, int vend,
+                                               const Sampling& smp, unsigned pos) {
+  if constexpr (MODE == kModeSample) fold_tile_sample(p, a, vb, h, vend, smp, pos);
+  else fold_tile<MODE == kModeEnt, MASKED>(p, a, vb, h, vend);
+}
+
+constexpr int kWideThreads = 256;
+constexpr int kWideWStages = 3;
+constexpr int kWideHStages = 2;
+constexpr int kWideSmem = 152 * 1024;
+constexpr int kWideFoldSlot = 2048;   // bytes of LDS per wave for the fold's round trip
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Sequence position of the loads: load number i goes to stage i % S and
+// fetches chunk min(i, total - 1) (past the end the last chunk again, so
+// every barrier sees the same number of loads in flight).
+template <int S>
+struct LoadCursor {
+  int i, stage, pass, kci;
+  __device__ __forceinline__ void step(int total, int nch) {
+    stage = stage + 1 == S ? 0 : stage + 1;
+    if (i + 1 < total) {
+      ++i;
+      if (++kci == nch) {
+        kci = 0;
+        ++pass;
+      }
+    }
+  }
+};
+
+template <int TW, int Q, int R, int MODE>
+__device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int part, int Mg,
+                                          int row0, int h_bytes,
+                                          const unsigned short* __restrict__ H,
+                                          const unsigned short* __restrict__ W,
+                                          const int32_t* __restrict__ rows, unsigned char* smem,
+                                          float* __restrict__ ws_m, float* __restrict__ ws_s,
+                                          int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
+                                          float* __restrict__ ws_z, const Sampling smp) {
+  using RP = typename std::conditional<MODE == kModeSample, SPartial, Partial>::type;
+  constexpr int TH = 4 * Q + R;          // activation tiles of the group
+  constexpr int QR = Q + R;              // activation tiles this wave multiplies
+  constexpr int WROWS = TW * 32;         // weight rows per pass
+  constexpr int WBUF = WROWS * kRB, HBUF = TH * 32 * kRB;
+  constexpr int XP = TW / 4;             // weight tiles per remaining activation tile per wave
+  constexpr int KS = kKC / 16;           // MFMA K steps per chunk
+  static_assert(TW % 4 == 0 && Q >= 1 && R >= 0 && R < 4 && TH <= kWideMaxTiles, "wide layout");
+  static_assert(kWideWStages * WBUF + kWideHStages * HBUF <= kWideSmem, "wide LDS");
+  static_assert(R * 4 * 32 * static_cast<int>(sizeof(RP)) <= kWideSmem, "merge area");
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, lh = lane >> 5;
+  const int row_bytes = hidden * 2;
+  const int t16 = (V + 15) >> 4;
+  const int v_lo = static_cast<int>(static_cast<long long>(part) * t16 / nparts) * 16;
+  const int v_hi = min(static_cast<int>(static_cast<long long>(part + 1) * t16 / nparts) * 16, V);
+  const int npass = max(v_hi - v_lo, 0) / WROWS + ((max(v_hi - v_lo, 0) % WROWS) != 0);
+  const int nch = hidden / kKC;
+  const int total = npass * nch;
+  const int rot = ((part >> 3) * nch / 32) % nch;
+  unsigned char* const hbase = smem + kWideWStages * WBUF;
+
+  // running partials: own tiles (complete over the part) and the remaining
+  // tiles (this wave's weight tiles only; merged across waves at the end)
+  RP run[Q], runx[R > 0 ? R : 1];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    if constexpr (MODE == kModeSample) run[t] = empty_spartial();
+    else run[t] = empty_partial();
+  }
+#pragma unroll
+  for (int t = 0; t < (R > 0 ? R : 1); ++t) {
+    if constexpr (MODE == kModeSample) runx[t] = empty_spartial();
+    else runx[t] = empty_partial();
+  }
+  // activation row of this lane in each tile it multiplies (own, then the
+  // remaining ones), and its block position (temperature sampling only)
+  int hrow[QR];
+#pragma unroll
+  for (int t = 0; t < QR; ++t) hrow[t] = (t < Q ? w * Q + t : 4 * Q + t - Q) * 32 + ln;
+  unsigned pos[QR];
+  if constexpr (MODE == kModeSample) {
+#pragma unroll
+    for (int t = 0; t < QR; ++t)
+      pos[t] = static_cast<unsigned>(rows[row0 + min(hrow[t], Mg - 1)] % smp.B);
+  }
+
+  if (total > 0) {
+    // ---- loads: 16-byte pieces straight into LDS, 8 rows per instruction;
+    // instruction p of wave w fills rows 8 (4p + w) .. +8 of a stage, lane
+    // l the XOR-swizzled slot of row 8 (4p + w) + l / 8
+    const int r8 = lane >> 3;
+    const int ls = (lane & 7) ^ r8 ^ (w & 1);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(W) + static_cast<size_t>(v_lo) * hidden, 0,
+        (v_hi - v_lo) * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
+    const int wv = (8 * w + r8) * row_bytes + ls * 16;
+    int hv[TH];
+#pragma unroll
+    for (int p = 0; p < TH; ++p)
+      hv[p] = rows[row0 + min(8 * (4 * p + w) + r8, Mg - 1)] * row_bytes + ls * 16;
+    LoadCursor<kWideWStages> lw{0, 0, 0, 0};
+    LoadCursor<kWideHStages> lhc{0, 0, 0, 0};
+    auto kc_of = [&](int kci) __attribute__((always_inline)) {
+      const int kc = kci + rot;
+      return kc >= nch ? kc - nch : kc;
+    };
+    auto issue_w = [&]() __attribute__((always_inline)) {
+      unsigned char* dst = smem + lw.stage * WBUF;
+      const int so = lw.pass * WROWS * row_bytes + kc_of(lw.kci) * kRB;
+#pragma unroll
+      for (int p = 0; p < TW; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + w) * 1024), 16, wv,
+                                                 so + 32 * p * row_bytes, 0, kWeightAux);
+      lw.step(total, nch);
+    };
+    auto issue_h = [&]() __attribute__((always_inline)) {
+      unsigned char* dst = hbase + lhc.stage * HBUF;
+      const int so = kc_of(lhc.kci) * kRB;
+#pragma unroll
+      for (int p = 0; p < TH; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, LOPA_LDS(dst + (4 * p + w) * 1024), 16, hv[p],
+                                                 so, 0, 0);
+      lhc.step(total, nch);
+    };
+
+    // ---- fragments of K step j of the chunk in W stage sw / H stage sh
+    struct Frags {
+      u16x8 w[TW], h[QR], xw[XP];
+    };
+    auto read_frags = [&](int sw, int sh, int j, Frags& f) __attribute__((always_inline)) {
+      const unsigned char* wb = smem + sw * WBUF;
+      const unsigned char* hb = hbase + sh * HBUF;
+      const int sl = 2 * j + lh;   // logical slot: K values 16j + 8lh .. +8
+#pragma unroll
+      for (int n = 0; n < TW; ++n) {
+        const int r = n * 32 + ln;
+        f.w[n] = *reinterpret_cast<const u16x8*>(wb + r * kRB + swz<kKC>(r, sl) * 16);
+      }
+#pragma unroll
+      for (int t = 0; t < QR; ++t)
+        f.h[t] = *reinterpret_cast<const u16x8*>(hb + hrow[t] * kRB + swz<kKC>(hrow[t], sl) * 16);
+      // weight tiles w + 4k: this wave's pairs with the remaining tiles
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int k = 0; k < XP; ++k) {
+          const int r = (w + 4 * k) * 32 + ln;
+          f.xw[k] = *reinterpret_cast<const u16x8*>(wb + r * kRB + swz<kKC>(r, sl) * 16);
+        }
+      }
+    };
+
+    f32x16 acc[Q][TW], accx[R > 0 ? R : 1][XP];
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+#pragma unroll
+      for (int n = 0; n < TW; ++n) acc[t][n] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < (R > 0 ? R : 1); ++t)
+#pragma unroll
+      for (int k = 0; k < XP; ++k) accx[t][k] = f32x16{};
+
+    // NL: live weight tiles of the pass (the others are neither multiplied
+    // nor folded); the remaining tiles' pairs always run (a pair past the
+    // part reads zeros and its entries are dropped by the masked fold)
+    auto mfma_step = [&](auto nl_c, const Frags& f) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nl_c)::value;
+#pragma unroll
+      for (int t = 0; t < Q; ++t)
+#pragma unroll
+        for (int n = 0; n < NL; ++n)
+          acc[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, f.h[t]), acc[t][n],
+              0, 0, 0);
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int k = 0; k < XP; ++k)
+#pragma unroll
+          for (int t = 0; t < R; ++t)
+            accx[t][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, f.h[Q + t]),
+                accx[t][k], 0, 0, 0);
+      }
+    };
+
+    // An accumulator tile on its way to the fold passes through this wave's
+    // slot of LDS (volatile, so the round trip stays): the matrix registers
+    // that hold the accumulators are stored as they are, and the fold reads
+    // ordinary registers back, one tile at a time.
+    volatile f32x4* fslot =
+        reinterpret_cast<volatile f32x4*>(smem + kWideSmem + w * kWideFoldSlot) + lane;
+    auto through_lds = [&](const f32x16& a) __attribute__((always_inline)) {
+      f32x16 r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        fslot[64 * (q & 1)] = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        if (q & 1) {
+          const f32x4 u = fslot[0], v = fslot[64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[4 * (q - 1) + e] = u[e];
+            r[4 * q + e] = v[e];
+          }
+        }
+      }
+      return r;
+    };
+    // fold a pass's logits into the running partials (one tile at a time)
+    // and clear them
+    auto fold = [&](auto nl_c, auto masked_c, int pass) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nl_c)::value;
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int vb = v_lo + pass * WROWS;
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+          fold_tile_mode<MODE, MASKED>(run[t], through_lds(acc[t][n]), vb + n * 32, lh, v_hi, smp,
+                                       MODE == kModeSample ? pos[t] : 0u);
+          acc[t][n] = f32x16{};
+          // one tile at a time: interleaving the tiles' folds would move
+          // every accumulator out of the matrix registers at once
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+#pragma unroll
+          for (int k = 0; k < XP; ++k) {
+            const int vt = vb + 32 * (w + 4 * k);
+            fold_tile_mode<MODE, MASKED>(runx[t], through_lds(accx[t][k]), vt, lh, v_hi, smp,
+                                         MODE == kModeSample ? pos[Q + t] : 0u);
+            accx[t][k] = f32x16{};
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    };
+
+    // ---- prologue: W(0), H(0), W(1); the barrier; H(1), W(2).  At every
+    // barrier the activation chunk is issued before the weight chunk, so
+    // waiting for chunk c + 1 leaves only W(c + 2) in flight.
+    issue_w();
+    issue_h();
+    issue_w();
+    wait_vm_lgkm0<TW>();
+    raw_barrier();
+    issue_h();
+    issue_w();
+    // Fragments are read two K steps ahead: fr[j] holds step j of the chunk
+    // being computed (KS == 4 sets, indexed statically).
+    static_assert(KS == 4, "fragment ring");
+    Frags fr[KS];
+    int cw = 0, chs = 0;   // stages of the chunk being computed
+    read_frags(cw, chs, 0, fr[0]);
+    read_frags(cw, chs, 1, fr[1]);
+    // One chunk.  The barrier sits in step 2: by then every fragment of
+    // this chunk has been read (steps 2 and 3 at steps 0 and 1), so the
+    // chunk's stages are free for H(c + 2) and W(c + 3) once every wave has
+    // passed it; the two steps after it read the next chunk's first two
+    // steps while their MFMAs run.  (After the last chunk this re-loads the
+    // last chunk and reads stages that are not used: every wave takes the
+    // same steps.)
+    auto chunk = [&](auto nl_c) __attribute__((always_inline)) {
+      read_frags(cw, chs, 2, fr[2]);
+      mfma_step(nl_c, fr[0]);
+      read_frags(cw, chs, 3, fr[3]);
+      mfma_step(nl_c, fr[1]);
+      // this wave's loads of chunk c + 1 have landed and its reads of chunk
+      // c are done: after the barrier, every wave's
+      wait_vm_lgkm0<TW>();
+      raw_barrier();
+      issue_h();
+      issue_w();
+      cw = cw + 1 == kWideWStages ? 0 : cw + 1;
+      chs = chs + 1 == kWideHStages ? 0 : chs + 1;
+      read_frags(cw, chs, 0, fr[0]);
+      mfma_step(nl_c, fr[2]);
+      read_frags(cw, chs, 1, fr[1]);
+      mfma_step(nl_c, fr[3]);
+    };
+    auto run_pass = [&](auto nl_c, auto masked_c, int pass) __attribute__((always_inline)) {
+      for (int kk = 0; kk < nch; ++kk) chunk(nl_c);
+      fold(nl_c, masked_c, pass);
+    };
+    for (int pass = 0; pass + 1 < npass; ++pass)
+      run_pass(std::integral_constant<int, TW>{}, std::false_type{}, pass);
+    {
+      const int rem = v_hi - v_lo - (npass - 1) * WROWS;   // rows of the last pass, 1..WROWS
+      const int nl = (rem + 31) / 32;
+      static_assert(TW == 4 || TW == 8, "last-pass dispatch");
+#define LOPA_LAST(N)                                                                   \
+  case N:                                                                              \
+    run_pass(std::integral_constant<int, N>{}, std::true_type{}, npass - 1);           \
+    break;
+      if constexpr (TW == 4) {
+        switch (nl) { LOPA_LAST(1) LOPA_LAST(2) LOPA_LAST(3) default: LOPA_LAST(4) }
+      } else {
+        switch (nl) {
+          LOPA_LAST(1) LOPA_LAST(2) LOPA_LAST(3) LOPA_LAST(4) LOPA_LAST(5) LOPA_LAST(6)
+          LOPA_LAST(7) default: LOPA_LAST(8)
+        }
+      }
+#undef LOPA_LAST
+    }
+    wait_vmcnt<0>();   // no load may still target LDS when it is reused below
+  }
+  __syncthreads();
+  // the two lane halves of every row
+#pragma unroll
+  for (int t = 0; t < Q; ++t) run[t] = merge(run[t], shfl_xor(run[t], 32));
+#pragma unroll
+  for (int t = 0; t < R; ++t) runx[t] = merge(runx[t], shfl_xor(runx[t], 32));
+  // own rows: complete partials; remaining rows: merged over the four waves
+  if (lh == 0) {
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const int r = (w * Q + t) * 32 + ln;
+      if (r < Mg) {
+        const size_t o = static_cast<size_t>(row0 + r) * nparts + part;
+        ws_m[o] = run[t].m;
+        ws_s[o] = run[t].s;
+        ws_i[o] = run[t].i;
+        if constexpr (MODE == kModeEnt) ws_t[o] = run[t].t;
+        if constexpr (MODE == kModeSample) {
+          ws_t[o] = run[t].g;
+          ws_z[o] = run[t].z;
+        }
+      }
+    }
+  }
+  if constexpr (R > 0) {
+    RP* xm = reinterpret_cast<RP*>(smem);   // [R][4 waves][32 rows]
+    if (lh == 0) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) xm[(t * 4 + w) * 32 + ln] = runx[t];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * 32; i += kWideThreads) {
+      const int t = i >> 5, l = i & 31;
+      const int r = (4 * Q + t) * 32 + l;
+      if (r < Mg) {
+        RP p = xm[(t * 4) * 32 + l];
+#pragma unroll
+        for (int x = 1; x < 4; ++x) p = merge(p, xm[(t * 4 + x) * 32 + l]);
+        const size_t o = static_cast<size_t>(row0 + r) * nparts + part;
+        ws_m[o] = p.m;
+        ws_s[o] = p.s;
+        ws_i[o] = p.i;
+        if constexpr (MODE == kModeEnt) ws_t[o] = p.t;
+        if constexpr (MODE == kModeSample) {
+          ws_t[o] = p.g;
+          ws_z[o] = p.z;
+        }
+      }
+    }
+  }
+}
+
+// kHeadParts workgroups of 256 threads, one per compute unit.  Row groups as
+// in k_lmhead_mfma: the groups of one vocabulary part take consecutive blocks
+// of the same XCD (block b runs on XCD b mod 8).  Returns at once when the
+// narrow kernel serves the row count.
+template <int MODE>
+__global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int h_bytes,
+              const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
+              const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
+              const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
+              float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
+              float* __restrict__ ws_z, const Sampling smp) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideSmem + 4 * kWideFoldSlot];
+  const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
+  if (!wide_takes(M)) return;
+  const WideGroups g = wide_groups(M);
+  const int b = blockIdx.x;
+  const int q = b >> 3;
+  const int group = q % g.groups;
+  const int part = (q / g.groups) * 8 + (b & 7);
+  const int row0 = group * g.th * 32;
+  if (part >= g.nparts || row0 >= M) return;
+  const int Mg = min(M - row0, g.th * 32);
+#define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
+                  ws_t, ws_z, smp
+  switch (g.th) {   // the layouts wide_takes() can reach
+    case 5: wide_body<8, 1, 1, MODE>(LOPA_ARGS); break;
+    case 6: wide_body<8, 1, 2, MODE>(LOPA_ARGS); break;
+    case 9: wide_body<4, 2, 1, MODE>(LOPA_ARGS); break;
+    default: wide_body<4, 3, 1, MODE>(LOPA_ARGS); break;
   }
 #undef LOPA_ARGS
 }
@@ -587,7 +1127,9 @@ k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
   const int m = blockIdx.x;
   const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
   if (m >= M) return;
-  if (mfma) ntiles = head_groups(M).nparts;
+  // mfma: 0 the plain kernel ran, 1 the narrow kernel alone, 2 both MFMA
+  // kernels (the wide one serving the row counts wide_takes() names)
+  if (mfma) ntiles = head_nparts(M, mfma == 2);
   RP p;
   if constexpr (MODE == kModeSample) p = empty_spartial();
   else p = empty_partial();
@@ -620,6 +1162,16 @@ k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
 
 }  // namespace lopa
 
+// The wide kernel is launched beside the narrow one when the device-side row
+// count may reach one it serves (more than kHeadNarrowRows rows; confidence
+// and entropy modes, no full logits requested).
+template <int MODE>
+static bool wide_serves(const lopa::HeadPlan& p, int hidden, const float* logits_out) {
+  (void)hidden;
+  return MODE != lopa::kModeSample && p.mfma && p.m_max > lopa::kHeadNarrowRows &&
+         logits_out == nullptr;
+}
+
 // All three entry points.  Workspace planes of m_max x ntiles: max, sum,
 // index, then the entropy term or the perturbed best score, then the scaled
 // logit of the sample.
@@ -648,9 +1200,24 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
   const unsigned short* Wb = static_cast<const unsigned short*>(W);
   const int h_bytes = p.m_max * hidden * 2;   // H is [nb_max][B][hidden]
   if (p.mfma) {
+    // the weight range of one vocabulary part (plus one pass of overrun) is
+    // addressed with 32-bit byte offsets
+    if (head_part_bytes_max(*dims) >= (1LL << 31)) return LOPA_ERR_UNSUPPORTED;
+    // the row count lives on the device: when it may exceed what the narrow
+    // kernel serves, both kernels are launched and the one not needed
+    // returns at once.  Full logits and temperature sampling are served by
+    // the narrow kernel only (it takes any row count).
+    const bool wide = wide_serves<MODE>(p, hidden, logits_out);
     hipLaunchKernelGGL(k_lmhead_mfma<MODE>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V,
-                       hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm, wsum, wi,
-                       wt, wz, smp, logits_out);
+                       hidden, nb_max, p.m_max, wide ? 1 : 0, h_bytes, Hb, Wb, rows, row_ptr, nb,
+                       wm, wsum, wi, wt, wz, smp, logits_out);
+    LOPA_LAUNCH_CHECK();
+    if constexpr (MODE != kModeSample) {
+      if (wide)
+        hipLaunchKernelGGL(k_lmhead_wide<MODE>, dim3(kHeadParts), dim3(kWideThreads), 0, stream,
+                           V, hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm,
+                           wsum, wi, wt, wz, smp);
+    }
   } else {
     const dim3 grid(p.ntiles, p.m_max);
     if (dims->dtype == LOPA_F32) {
@@ -665,8 +1232,9 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
     }
   }
   LOPA_LAUNCH_CHECK();
+  const int served = !p.mfma ? 0 : (wide_serves<MODE>(p, hidden, logits_out) ? 2 : 1);
   hipLaunchKernelGGL(k_lmhead_merge<MODE>, dim3(p.m_max), dim3(256), 0, stream, V, p.ntiles,
-                     p.mfma ? 1 : 0, nb_max, p.m_max, rows, row_ptr, nb, wm, wsum, wi, wt, wz,
+                     served, nb_max, p.m_max, rows, row_ptr, nb, wm, wsum, wi, wt, wz,
                      conf, arg, ent);
   LOPA_LAUNCH_CHECK();
   return LOPA_OK;

@@ -189,3 +189,50 @@ def test_model_calls_reject_null_and_small_workspace():
     # the commit must fit the cache
     assert L.lopa_model_commit(ctypes.byref(d), ctypes.byref(md), fake, fake, fake, fake, fake,
                                40, 30, None) == -1
+
+
+@pytest.mark.parametrize("shape", [dict(Hq=8, Hkv=2, B=16, k_max=2, d=128),
+                                   dict(Hq=28, Hkv=4, B=32, k_max=4, d=128),
+                                   dict(Hq=28, Hkv=4, B=32, k_max=8, d=128),
+                                   dict(Hq=4, Hkv=1, B=16, k_max=2, d=128)])
+def test_workspace_never_shrinks_as_the_prefix_grows(shape):
+    """A decoded sequence grows its prefix block by block and keeps one
+    workspace: the size for a prefix must cover every shorter one, although
+    the split count of the attention partials is not monotone in the prefix
+    (8 q-heads over 2 KV heads, block 16, 3 branches: 4 splits at prefix 448
+    but 3 at 512)."""
+    prev = 0
+    for L in range(0, 4097, 32):
+        n = lopa.workspace_bytes(_dims(L=L, V=4096, **shape))
+        assert n >= prev, (L, n, prev)
+        prev = n
+
+
+def test_offsets_past_32_bits_rejected():
+    """The MFMA kernels address K/V and the weight range of a vocabulary part
+    with 32-bit byte offsets: shapes past that are refused, not computed
+    wrongly."""
+    L = lopa.lib()
+    fake = ctypes.c_void_p(256)
+    # prefix K/V of 2^20 keys x 8 KV heads x 128 x 2 bytes = 2^31 bytes
+    d = _dims(L=1 << 20, Hq=8, Hkv=8, B=16, k_max=0)
+    assert L.lopa_branch_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                              1 << 40, None) == -2
+    # 2^22 vocabulary rows of 65536 bf16 values over 256 parts: 16384 rows
+    # (+ one pass of overrun) of 128 KiB each per part
+    d = _dims(Hq=512, Hkv=8, d=128, V=1 << 22, B=16, k_max=0)
+    assert L.lopa_lmhead_conf(ctypes.byref(d), *([fake] * 7), None, fake, 1 << 40, None) == -2
+
+
+def test_model_slot_table_overflow_rejected():
+    """A projection whose single unit spans all 256 workgroups (hidden 256,
+    inter 16384: the down projection's K range is 256 chunks) would need 256
+    slots, more than the consumers' one-byte slot table counts."""
+    d = _dims(L=40, B=16, Hq=4, Hkv=2, d=64, V=1000, k_max=0)
+    out = lopa.ModelLayout()
+    md = _model_dims(inter=16384)
+    assert lopa.lib().lopa_model_layout_of(ctypes.byref(d), ctypes.byref(md),
+                                           ctypes.byref(out)) == -2
+    md = _model_dims(inter=8192)
+    assert lopa.lib().lopa_model_layout_of(ctypes.byref(d), ctypes.byref(md),
+                                           ctypes.byref(out)) == 0
