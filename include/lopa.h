@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LOPA_ABI_VERSION 1
+#define LOPA_ABI_VERSION 2
 #define LOPA_MASK_TOKEN (-1)
 #define LOPA_MAX_BLOCK 64        /* B <= 64: one block fits one wavefront      */
 #define LOPA_MAX_BRANCHES 16     /* nb_max = 1 + k_max <= 16                   */
@@ -61,7 +61,9 @@ typedef enum {
   LOPA_ERR_INVALID = -1,      /* null pointer, bad size, k > k_max, ...        */
   LOPA_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle     */
   LOPA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
-  LOPA_ERR_HIP = -4           /* the HIP runtime rejected a launch             */
+  LOPA_ERR_HIP = -4,          /* the HIP runtime rejected a launch             */
+  LOPA_ERR_TOO_LARGE = -5     /* more scratch than the fixed array holds
+                                 (lopa_lmhead_conf_noalloc)                    */
 } lopa_status;
 
 typedef enum { LOPA_F32 = 0, LOPA_BF16 = 1 } lopa_dtype;
@@ -178,6 +180,28 @@ int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
                      const int32_t* nb, float* conf, int32_t* arg,
                      float* logits_out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * lopa_lmhead_conf without a workspace, for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results as
+ * lopa_lmhead_conf, bit for bit, with its partials in a fixed array inside
+ * the library (5 MiB per device, held by every device the library runs on
+ * until the process ends).  The call itself allocates nothing; on its first
+ * call on a device it looks up that device's copy of the array.
+ *   Returns LOPA_ERR_TOO_LARGE (nothing launched) when the partials would not
+ *   fit: never for bfloat16 shapes the MFMA kernels take; for the float32
+ *   path when nb_max*B x ceil(V / 256) > 262144.
+ *   Every call on a device uses that device's one array and leaves it
+ *   holding its partials: calls that overlap on one device (different
+ *   streams, or host threads without ordering) race.  Calls ordered on one
+ *   stream are safe; nothing has to be cleared between them (each call writes
+ *   every partial it reads).
+ */
+int lopa_lmhead_conf_noalloc(const lopa_dims* dims, const void* H, const void* W,
+                             const int32_t* rows, const int32_t* row_ptr,
+                             const int32_t* nb, float* conf, int32_t* arg,
+                             float* logits_out, hipStream_t stream);
 
 /*
  * lopa_lmhead_conf plus, for every listed row, the normalised entropy of the

@@ -28,7 +28,7 @@ MAX_BLOCK = 64
 MAX_BRANCHES = 16
 
 STATUS = {0: "LOPA_OK", -1: "LOPA_ERR_INVALID", -2: "LOPA_ERR_UNSUPPORTED",
-          -3: "LOPA_ERR_WORKSPACE", -4: "LOPA_ERR_HIP"}
+          -3: "LOPA_ERR_WORKSPACE", -4: "LOPA_ERR_HIP", -5: "LOPA_ERR_TOO_LARGE"}
 
 
 class Dims(ctypes.Structure):
@@ -86,6 +86,8 @@ _SIGS = {
                          ctypes.c_int),
     "lopa_lmhead_conf": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                          ctypes.c_int),
+    "lopa_lmhead_conf_noalloc": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                                 ctypes.c_int),
     "lopa_branch_select": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                            ctypes.c_int),
     "lopa_lmhead_conf_ent": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -217,6 +219,19 @@ def lopa_lmhead_conf(dims, H, W, rows, row_ptr, nb, conf, arg, logits_out, ws,
         _ptr(arg, i32, "arg"), _ptr(logits_out, torch.float32, "logits_out"),
         _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def lopa_lmhead_conf_noalloc(dims, H, W, rows, row_ptr, nb, conf, arg, logits_out=None,
+                             stream=None) -> None:
+    """lopa_lmhead_conf with its partials in the library's fixed device array
+    (no workspace argument; allocates nothing)."""
+    import torch
+    a = _act_dtype(dims)
+    i32 = torch.int32
+    _check("lopa_lmhead_conf_noalloc", lib().lopa_lmhead_conf_noalloc(
+        ctypes.byref(dims), _ptr(H, a, "H"), _ptr(W, a, "W"), _ptr(rows, i32, "rows"),
+        _ptr(row_ptr, i32, "row_ptr"), _ptr(nb, i32, "nb"), _ptr(conf, torch.float32, "conf"),
+        _ptr(arg, i32, "arg"), _ptr(logits_out, torch.float32, "logits_out"), _stream(stream)))
 
 
 def lopa_branch_select(dims, nb, br_mask, br_tok, conf, arg, bconf, winner, tok_next,

@@ -12,6 +12,8 @@ extern "C" const char* lopa_status_string(int status) {
     case LOPA_ERR_UNSUPPORTED: return "valid arguments outside what the kernels support";
     case LOPA_ERR_WORKSPACE: return "workspace missing or smaller than lopa_workspace_bytes()";
     case LOPA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case LOPA_ERR_TOO_LARGE:
+      return "the call needs more than the library's fixed scratch array holds";
     default: return "unknown lopa status";
   }
 }

@@ -28,6 +28,7 @@
 //                   through L2.
 //   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
 //                   per vocabulary entry, FMA dot products.
+#include <mutex>
 #include <type_traits>
 
 #include "lopa_common.hpp"
@@ -1269,4 +1270,47 @@ extern "C" int lopa_lmhead_sample(const lopa_dims* dims, float temperature, uint
                            static_cast<unsigned>(seed >> 32), dims ? dims->B : 1};
   return lmhead_launch<lopa::kModeSample>(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr, smp,
                                           logits_out, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free LM head (for callers that cannot allocate): the partials
+// live in a fixed device array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+
+// 5 MiB: every bfloat16 MFMA shape (m_max <= 1024 rows x 256 vocabulary parts
+// x 20 bytes) fits; the float32 path fits while m_max x ceil(V / 256) <= 262144.
+constexpr size_t kScratchBytes = static_cast<size_t>(5) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices];   // device address of `scratch` on each device, once looked up
+}  // namespace
+
+extern "C" int lopa_lmhead_conf_noalloc(const lopa_dims* dims, const void* H, const void* W,
+                                        const int32_t* rows, const int32_t* row_ptr,
+                                        const int32_t* nb, float* conf, int32_t* arg,
+                                        float* logits_out, hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (!H || !W || !rows || !row_ptr || !nb || !conf || !arg) return LOPA_ERR_INVALID;
+  if (lopa::lmhead_workspace_bytes(*dims) > kScratchBytes) return LOPA_ERR_TOO_LARGE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return LOPA_ERR_HIP;
+  void* ws = nullptr;
+  {
+    // the array's address on the current device, looked up once per device
+    // (in host code `scratch` names a host-side stand-in, not device memory)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return LOPA_ERR_HIP;
+      g_scratch[dev] = ptr;
+    }
+    ws = g_scratch[dev];
+  }
+  return lmhead_launch<lopa::kModeConf>(dims, H, W, rows, row_ptr, nb, conf, arg, nullptr,
+                                        lopa::Sampling{}, logits_out, ws, kScratchBytes, stream);
 }

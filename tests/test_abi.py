@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lopa.abi_version() == 1
-    for s in (0, -1, -2, -3, -4, 7):
+    assert lopa.abi_version() == 2
+    for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lopa.status_string(s), str) and lopa.status_string(s)
 
 
@@ -236,3 +236,18 @@ def test_model_slot_table_overflow_rejected():
     md = _model_dims(inter=8192)
     assert lopa.lib().lopa_model_layout_of(ctypes.byref(d), ctypes.byref(md),
                                            ctypes.byref(out)) == 0
+
+
+def test_noalloc_head_rejects_before_any_launch():
+    """The allocation-free LM head checks its arguments, and that its partials
+    fit the library's fixed 5 MiB array, before touching the HIP runtime."""
+    L = lopa.lib()
+    fake = ctypes.c_void_p(256)
+    d = _dims()
+    assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), None, *([fake] * 7), None) == -1
+    assert L.lopa_lmhead_conf_noalloc(None, *([fake] * 8), None) == -1
+    # float32 path over a 152064-entry vocabulary with 16 x 64 rows: 1024 x 594
+    # partials of 20 bytes (12 MB) do not fit
+    d = _dims(dtype=lopa.F32, B=64, k_max=15)
+    assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), *([fake] * 8), None) == -5
+    assert "scratch" in lopa.status_string(-5)
