@@ -2,21 +2,38 @@
 model_decode_sequence) against oracle/model_oracle (initial_pass,
 decode_step, forward).
 
-The GPU forward and the oracle's agree to bf16 rounding noise (see
-test_gpu_model.py); from identical states the confidences of one step
-differ by up to 1.5e-2 on these geometries (measured).  A whole decoding
-trajectory therefore follows the oracle's only while every decision is clear
-by more than that, which few blocks are for long.  So each GPU step is
-checked from the GPU's own state: the oracle takes one step from the state
-the GPU logged (the explore stage then sees identical inputs and decides
-identically), and whenever that step's outcome is clear-cut -- the top-2
-logit gap behind every token it fills > FILL and the winner's
-branch-confidence margin > GAP -- the GPU's next tokens must equal the
-oracle's, its next confidences agree to GAP and its next argmax tokens
-agree where their logit gap is > FILL.  The committed prefix of every layer
-is compared with the oracle's forward of the GPU's decoded tokens, to the
-forward's tolerance.
+Tolerances.  The GPU forward and the oracle's differ by bf16 rounding noise
+(test_gpu_model.py).  tests/golden/forward_noise.json holds what that noise
+does to the LM head under the rounding-noise model (every value entering a
+bf16 rounding point perturbed by 2^-16 relative, run through the oracle),
+over a block's first two passes: the largest change of a row's confidence
+("conf"), of a branch confidence ("branch": the mean confidence of the rows
+the branch leaves masked) and of a logit relative to the row's top logit
+("lead").  Allowed, with a factor 2 of margin: CONF = 2 conf for a row
+confidence (4.3e-2 on the wider geometry: this exceeds the 2e-2 that the
+branch step meets from given hidden rows, because here the hidden rows
+themselves carry the forward's rounding noise); LEAD = 2 lead for a token
+(its top-2 logit gap must exceed LEAD for the GPU to be held to the same
+token); two branches' order can flip only when their gap is below
+GAP = 2 (2 branch), both moving.
+
+A whole trajectory follows the oracle's only while every decision clears
+those gaps, so each GPU step is checked from the GPU's own state: the oracle
+takes one step from the state the GPU logged (the explore stage sees
+identical inputs and builds identical branches), and
+  * the GPU's next tokens are one of the step's branches, b;
+  * the oracle's branch confidence of b is within GAP of the best one, and b
+    is the oracle's winner whenever the winner leads by more than GAP
+    ("clear-cut" steps: at least MIN_CLEAR of every block's steps);
+  * the GPU's next confidences are within CONF of the oracle's for branch b,
+    its next argmax tokens equal the oracle's where their lead exceeds LEAD
+    and lie within LEAD of the top logit elsewhere.
+The committed prefix of every layer is compared with the oracle's forward
+of the GPU's decoded tokens to the forward's bound for that geometry.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,28 +43,20 @@ from lookahead_decoding_amd.model import (Model, ModelDecodeBuffers, model_decod
                                           model_decode_sequence, model_dims)
 from oracle import lopa_oracle as O
 from oracle import model_oracle as MO
+from _model_cases import DECODE_CASES as CASES
+from _model_cases import block as _block
 
 pytestmark = pytest.mark.gpu
 M = O.MASK
-FILL = 0.1    # logit gap behind a filled token
-GAP = 3e-2    # confidence gaps: twice the largest difference measured from identical states
+with open(os.path.join(os.path.dirname(__file__), "golden", "forward_noise.json")) as _f:
+    _NOISE = json.load(_f)
+MIN_CLEAR = 0.4   # share of a block's steps whose winner leads by more than GAP
 
 
-def _block(seed, B, m, V):
-    rng = np.random.default_rng(100 + seed)
-    tok = rng.integers(0, V - 1, B).astype(np.int32)
-    tok[rng.choice(B, m, replace=False)] = M
-    return tok
-
-
-CASES = [
-    # name, geometry (L, B, k, Hq, Hkv, d, inter, V, layers), masked, seed
-    ("small-1", (40, 16, 3, 4, 2, 64, 512, 1000, 2), 10, 1),
-    ("small-4", (40, 16, 3, 4, 2, 64, 512, 1000, 2), 10, 4),
-    ("small-5", (40, 16, 3, 4, 2, 64, 512, 1000, 2), 10, 5),
-    ("mfma-1", (64, 32, 4, 8, 2, 128, 1024, 2000, 2), 16, 1),
-    ("mfma-2", (64, 32, 4, 8, 2, 128, 1024, 2000, 2), 16, 2),
-]
+def _tols(name):
+    """(CONF, LEAD, GAP) of the geometry ``name`` belongs to."""
+    g = _NOISE["decode"][name.split("-")[0]]
+    return 2 * g["conf"], 2 * g["lead"], 2 * (2 * g["branch"])
 
 
 def _setup(geo, seed, extra_rows=0):
@@ -64,41 +73,62 @@ def _logs(m, B):
              torch.zeros(m + 1, B, dtype=torch.int32, device="cuda")))
 
 
-def _check_block(what, seed, cfg, L, layers, prefix, W, tok0, k, tau, nb_max, log, state_log):
-    """Check the GPU's initial pass and every clear-cut step from the GPU's
-    own states.  Returns (steps checked, steps taken, the final tokens)."""
+def _check_block(what, tols, seed, cfg, L, layers, prefix, W, tok0, k, tau, nb_max, log,
+                 state_log):
+    """Check the GPU's initial pass and every step from the GPU's own states.
+    Returns (clear-cut steps, steps taken, the final tokens)."""
+    CONF, LEAD, GAP = tols
     got_tok = log.cpu().numpy()
     got_conf, got_arg = state_log[0].cpu().numpy(), state_log[1].cpu().numpy()
-    conf0, arg0, margin, _ = MO.initial_pass(seed, cfg, L, tok0, layers, prefix, W)
-    masked = tok0 == M
-    assert np.abs(got_conf[0][masked] - conf0[masked]).max(initial=0) <= GAP, f"{what}: conf0"
-    sure = masked & (margin > FILL)
-    assert np.array_equal(got_arg[0][sure], arg0[sure]), f"{what}: initial tokens"
+    B = len(tok0)
+    conf0, arg0, _, out0 = MO.initial_pass(seed, cfg, L, tok0, layers, prefix, W)
+    masked = np.flatnonzero(tok0 == M)
+    _check_rows(f"{what}: initial pass", got_conf[0][masked], got_arg[0][masked],
+                out0.H[0, masked], W, CONF, LEAD)
     tok, conf, arg = tok0.copy(), got_conf[0], got_arg[0]
-    checked = steps = 0
+    margin = np.full(B, np.inf)        # decode_step's fill statistic only
+    clear = steps = 0
     for s in range(len(got_tok)):
         if not np.any(tok == M):
             break
         steps += 1
-        st, (ntok, nconf, narg, nmargin), _, _, br, bmargin = MO.decode_step(
-            seed, cfg, L, tok, conf, arg, margin, k, tau, nb_max, layers, prefix, W)
-        # whatever the noise, the GPU's next tokens are one of the step's branches
+        st, _, out, w, br, _ = MO.decode_step(seed, cfg, L, tok, conf, arg, margin, k, tau,
+                                              nb_max, layers, prefix, W)
         took = [b for b in range(br.nb) if np.array_equal(br.br_tok[b], got_tok[s])]
         assert took, f"{what}: step {s}: the tokens are none of the {br.nb} branches"
-        if st.fill_margin > FILL and st.win_margin > GAP:
-            assert np.array_equal(got_tok[s], ntok), f"{what}: step {s} tokens"
-            rem = ntok == M
-            d = np.abs(got_conf[s + 1][rem] - nconf[rem]).max(initial=0)
-            assert d <= GAP, f"{what}: step {s} confidences differ by {d:.3g}"
-            sure = rem & (nmargin > FILL)
-            assert np.array_equal(got_arg[s + 1][sure], narg[sure]), f"{what}: step {s} argmax"
-            checked += 1
-        # the logit gaps behind the argmax tokens of the branch the GPU took
-        B = len(tok)
-        margin = np.where(got_tok[s] == M, bmargin[took[0] * B:(took[0] + 1) * B], np.inf)
+        b = took[0]
+        # the oracle's branch confidences (mean confidence of the rows a branch leaves masked)
+        bconf = np.ones(br.nb)
+        for c in range(br.nb):
+            rows = np.flatnonzero(br.br_mask[c])
+            if rows.size:
+                bconf[c] = O.lmhead_conf(out.H[c, rows], W).conf.mean()
+        assert bconf[b] >= bconf.max() - GAP, f"{what}: step {s}: branch {b} far from the best"
+        if st.win_margin > GAP:
+            assert b == w, f"{what}: step {s}: winner {b}, the oracle's {w}"
+            clear += 1
+        rem = np.flatnonzero(br.br_mask[b])
+        _check_rows(f"{what}: step {s}", got_conf[s + 1][rem], got_arg[s + 1][rem],
+                    out.H[b, rem], W, CONF, LEAD)
         tok, conf, arg = got_tok[s], got_conf[s + 1], got_arg[s + 1]
     assert not np.any(tok == M), f"{what}: block not finished after {steps} steps"
-    return checked, steps, tok
+    return clear, steps, tok
+
+
+def _check_rows(what, conf_gpu, arg_gpu, H, W, CONF, LEAD):
+    """The GPU's confidences and argmax tokens of rows whose oracle hidden
+    rows are H."""
+    if not len(H):
+        return
+    head = O.lmhead_conf(H, W)
+    d = np.abs(conf_gpu - head.conf).max()
+    assert d <= CONF, f"{what}: confidences differ by {d:.3g}"
+    sure = head.margin > LEAD
+    assert np.array_equal(arg_gpu[sure], head.arg[sure]), f"{what}: argmax tokens"
+    lg = H @ W.astype(np.float64).T
+    for r in np.flatnonzero(~sure):
+        lead = lg[r].max() - lg[r, int(arg_gpu[r])]
+        assert lead <= LEAD, f"{what}: row {r}: token {int(arg_gpu[r])} {lead:.3g} below the top"
 
 
 @pytest.mark.parametrize("name,geo,m,seed", CASES, ids=[c[0] for c in CASES])
@@ -112,10 +142,10 @@ def test_gpu_model_decode_block(name, geo, m, seed):
     layers = [MO.synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
     prefix = [MO.synth_prefix(seed, cfg, l, dims.L) for l in range(cfg.n_layers)]
     W = MO.lm_head_weight(seed, cfg)
-    checked, steps, _ = _check_block(name, seed, cfg, dims.L, layers, prefix, W, tok,
-                                     dims.k_max, 0.9, dims.nb_max, log, state_log)
-    print(f"[model decode] {name}: {checked} of {steps} steps clear-cut and checked", flush=True)
-    assert checked >= 1, f"{name}: no step clear-cut"
+    clear, steps, _ = _check_block(name, _tols(name), seed, cfg, dims.L, layers, prefix, W,
+                                   tok, dims.k_max, 0.9, dims.nb_max, log, state_log)
+    print(f"[model decode] {name}: {clear} of {steps} steps clear-cut", flush=True)
+    assert clear >= MIN_CLEAR * steps, f"{name}: {clear} of {steps} steps clear-cut"
     # the log is complete: steps past the end repeat the final tokens
     got = log.cpu().numpy()
     assert np.all(got[steps - 1:] == got[steps - 1])
@@ -141,19 +171,22 @@ def test_gpu_model_decode_sequence_commits_every_layer():
         assert np.array_equal(g(model.Vp[l, :dims.L]), prefix[l][1])
     Lj = dims.L
     for j, tok0 in enumerate(blocks):
-        checked, steps, final = _check_block(f"block {j}", seed, cfg, Lj, layers, prefix, W,
-                                             tok0, dims.k_max, 0.9, dims.nb_max, *logs[j])
-        print(f"[model decode] block {j}: {checked} of {steps} steps checked", flush=True)
+        clear, steps, final = _check_block(f"block {j}", _tols("small"), seed, cfg, Lj, layers,
+                                           prefix, W, tok0, dims.k_max, 0.9, dims.nb_max,
+                                           *logs[j])
+        print(f"[model decode] block {j}: {clear} of {steps} steps clear-cut", flush=True)
+        assert clear >= MIN_CLEAR * steps, f"block {j}: {clear} of {steps} steps clear-cut"
         # the commit appended the keys and values of the decoded block: the
         # last pass's winner slot, whose input was the final tokens
         out = MO.forward(seed, cfg, Lj, final[None], layers, prefix)
         for l in range(cfg.n_layers):
-            for got, want in ((g(model.Kp[l, Lj:Lj + 16]), out.Kb[l, 0]),
-                              (g(model.Vp[l, Lj:Lj + 16]), out.Vb[l, 0])):
+            for got, want, key in ((g(model.Kp[l, Lj:Lj + 16]), out.Kb[l, 0], "K"),
+                                   (g(model.Vp[l, Lj:Lj + 16]), out.Vb[l, 0], "V")):
                 rms = float(np.sqrt(np.mean(want ** 2)))
                 err = np.abs(got - want)
-                assert err.max() <= 2.0 ** -4 * rms, (j, l)
-                assert err.mean() <= 2.0 ** -8 * rms * np.sqrt(cfg.n_layers), (j, l)
+                mx, mn = _NOISE["forward"]["commit"][key]
+                assert err.max() <= 2 * mx * rms, (j, l, key)
+                assert err.mean() <= 1.5 * mn * rms, (j, l, key)
         prefix = [(np.concatenate([prefix[l][0], out.Kb[l, 0]]),
                    np.concatenate([prefix[l][1], out.Vb[l, 0]])) for l in range(cfg.n_layers)]
         Lj += 16

@@ -8,6 +8,11 @@
 * Token keying: the same token at the same position gives the same vectors
   in every branch, anything else differs.
 * The decoding loop against cases with closed-form outcomes and invariants.
+* The explore-stage gaps against brute force: no perturbation of the
+  confidences smaller than the gaps (every sign corner of the box, tiny
+  blocks) changes what the explore stage builds, and one just past the rank
+  gap -- or past the threshold gap where crossing the threshold must matter
+  -- does.
 """
 import numpy as np
 import pytest
@@ -167,3 +172,86 @@ def test_sequence_appends_final_tokens_kv_and_later_blocks_see_it():
     assert np.array_equal(again.conf0, sq.blocks[1].conf0)
     orig = D.decode_block(replace(inp, tok=blocks[1]), 5, 3, 0.9)
     assert not np.array_equal(orig.conf0, sq.blocks[1].conf0)
+
+
+def _random_state(rng, gamma=False):
+    B = int(rng.integers(3, 8))
+    tok = rng.integers(0, 100, B).astype(np.int32)
+    masked = rng.random(B) < 0.7
+    masked[rng.integers(B)] = True
+    tok[masked] = O.MASK
+    # values on a coarse grid plus a small jitter: many near-ties, no exact ones
+    grid = np.linspace(0.1, 0.9, 9)
+    conf = rng.choice(grid, B) + rng.uniform(-2e-3, 2e-3, B)
+    conf[~masked] = 0.0
+    arg = rng.integers(0, 100, B).astype(np.int32)
+    tau = float(rng.choice(grid) + rng.uniform(-2e-3, 2e-3))
+    k = int(rng.integers(0, 5))
+    g = float(rng.choice(grid) + rng.uniform(-2e-3, 2e-3)) if gamma else None
+    return tok, conf, arg, tau, k, g
+
+
+def _built(tok, conf, arg, k, tau, g):
+    br = O.branch_build(tok, conf, arg, k, tau, k + 1, g)
+    M = int(br.row_ptr[-1])
+    return (br.nb, br.br_tok.tobytes(), br.br_mask.tobytes(), br.rows[:M].tobytes(),
+            br.row_ptr.tobytes())
+
+
+def _corners(n):
+    for bits in range(1 << n):
+        yield np.array([1.0 if bits >> i & 1 else -1.0 for i in range(n)])
+
+
+@pytest.mark.parametrize("gamma", [False, True])
+def test_explore_gaps_bound_every_perturbation_that_keeps_the_branches(gamma):
+    rng = np.random.default_rng(11 + gamma)
+    checked = 0
+    for _ in range(300):
+        tok, conf, arg, tau, k, g = _random_state(rng, gamma)
+        rank_gap, tau_gap = D._explore_gaps(tok, conf, tau, k, g)
+        r = 0.999 * min(rank_gap / 2, tau_gap)
+        m = np.flatnonzero(tok == O.MASK)
+        ref = _built(tok, conf, arg, k, tau, g)
+        for sgn in _corners(m.size):
+            c = conf.copy()
+            c[m] += r * sgn
+            assert _built(tok, c, arg, k, tau, g) == ref, (tok, conf, tau, k, g, sgn)
+        for _ in range(8):
+            c = conf.copy()
+            c[m] += rng.uniform(-r, r, m.size)
+            assert _built(tok, c, arg, k, tau, g) == ref
+        checked += 1
+    assert checked == 300
+
+
+def test_explore_gaps_are_tight():
+    """Just past the rank gap some sign corner changes the branches; just past
+    the threshold gap moving the nearest position alone across the threshold
+    does, whenever another position stays above it or the nearest was
+    above it with company."""
+    rng = np.random.default_rng(12)
+    rank_cases = tau_cases = 0
+    for _ in range(300):
+        tok, conf, arg, tau, k, _ = _random_state(rng)
+        rank_gap, tau_gap = D._explore_gaps(tok, conf, tau, k)
+        m = np.flatnonzero(tok == O.MASK)
+        ref = _built(tok, conf, arg, k, tau, None)
+        if np.isfinite(rank_gap) and 1.01 * rank_gap / 2 < tau_gap:
+            r = 1.01 * rank_gap / 2
+            changed = False
+            for sgn in _corners(m.size):
+                c = conf.copy()
+                c[m] += r * sgn
+                changed |= _built(tok, c, arg, k, tau, None) != ref
+            assert changed, (tok, conf, tau, k)
+            rank_cases += 1
+        near = m[np.argmin(np.abs(conf[m] - tau))]
+        above = m[conf[m] > tau]
+        if 1.01 * tau_gap < rank_gap / 2 and (above.size >= 2 or (above.size == 1 and
+                                                                   near not in above)):
+            c = conf.copy()
+            c[near] = tau + (1.01 * tau_gap if conf[near] < tau else -1.01 * tau_gap)
+            assert _built(tok, c, arg, k, tau, None) != ref
+            tau_cases += 1
+    assert rank_cases >= 50 and tau_cases >= 20, (rank_cases, tau_cases)

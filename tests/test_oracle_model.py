@@ -1,5 +1,8 @@
 """Pins of the layer-forward oracle (oracle/model_oracle.py), CPU only.
 
+* The whole forward (mask-token embedding row, two layers over per-layer
+  prefix caches, final RMSNorm), rounding points off, equals transformers'
+  Qwen2Model in float64.
 * The decoder layer, with the rounding points switched off, equals the
   transformers library's own Qwen2 decoder layer in float64 (an independent
   implementation) on the same weights, with the prefix keys/values in its
@@ -33,11 +36,11 @@ from transformers.models.qwen2.modeling_qwen2 import (  # noqa: E402
 CFG = MO.ModelCfg(n_layers=2, Hq=4, Hkv=2, d=64, inter=512, V=1000, mask_id=999)
 
 
-def _hf_config(cfg):
+def _hf_config(cfg, layers=1):
     c = Qwen2Config(hidden_size=cfg.hidden, intermediate_size=cfg.inter,
                     num_attention_heads=cfg.Hq, num_key_value_heads=cfg.Hkv,
-                    rms_norm_eps=cfg.rms_eps, rope_theta=cfg.rope_theta, num_hidden_layers=1,
-                    vocab_size=cfg.V)
+                    rms_norm_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
+                    num_hidden_layers=layers, vocab_size=cfg.V)
     c._attn_implementation = "eager"
     return c
 
@@ -85,6 +88,77 @@ def test_layer_equals_transformers_qwen2_layer(L):
     vals = cache.layers[0].values[0, :, L:, :].numpy().transpose(1, 0, 2)
     np.testing.assert_allclose(k[0], keys, rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(v[0], vals, rtol=1e-5, atol=1e-5)
+
+
+class _FixedRope(torch.nn.Module):
+    """Stands in for Qwen2Model's rotary module with the oracle's cos/sin (the
+    angles are pinned separately: transformers evaluates them in float32)."""
+
+    def __init__(self, cos, sin):
+        super().__init__()
+        self.cos, self.sin = cos, sin
+
+    def forward(self, x, position_ids):
+        return self.cos, self.sin
+
+
+@pytest.mark.parametrize("L", [0, 23])
+def test_forward_equals_transformers_qwen2_model(L):
+    """The whole stack -- the mask token's own embedding row, two decoder
+    layers over per-layer prefix caches, the final RMSNorm -- against
+    transformers' Qwen2Model in float64 with the rounding points off."""
+    seed, B = 41, 10
+    cfg = CFG
+    rng = np.random.default_rng(5)
+    tok = rng.integers(0, cfg.V - 1, B)
+    tok[[1, 4, 5, 8]] = O.MASK
+    layers = [MO.synth_layer(seed, cfg, l) for l in range(cfg.n_layers)]
+    prefix = [MO.synth_prefix(seed, cfg, l, L) for l in range(cfg.n_layers)]
+    got = MO.forward(seed, cfg, L, tok[None], layers, prefix, round_points=False).H[0]
+
+    from transformers.models.qwen2.modeling_qwen2 import Qwen2Model
+    hc = _hf_config(cfg, cfg.n_layers)
+    model = Qwen2Model(hc).double()
+    qd, kd = cfg.Hq * cfg.d, cfg.Hkv * cfg.d
+    t = lambda a: torch.tensor(np.ascontiguousarray(a), dtype=torch.float64)  # noqa: E731
+    with torch.no_grad():
+        model.embed_tokens.weight.copy_(t(MO.synth_rows(seed, cfg, MO.TENSOR_ID["embed"],
+                                                        np.arange(cfg.V))))
+        model.norm.weight.copy_(t(MO.synth_tensor(seed, 7, 0, 1, cfg.hidden, "norm")[0]))
+        for l, w in enumerate(layers):
+            layer = model.layers[l]
+            at = layer.self_attn
+            wqkv, wgu = w.wqkv.full(), w.wgu.full()
+            at.q_proj.weight.copy_(t(wqkv[:qd]))
+            at.q_proj.bias.copy_(t(w.bqkv[:qd]))
+            at.k_proj.weight.copy_(t(wqkv[qd:qd + kd]))
+            at.k_proj.bias.copy_(t(w.bqkv[qd:qd + kd]))
+            at.v_proj.weight.copy_(t(wqkv[qd + kd:]))
+            at.v_proj.bias.copy_(t(w.bqkv[qd + kd:]))
+            at.o_proj.weight.copy_(t(w.wo.full()))
+            layer.input_layernorm.weight.copy_(t(w.attn_norm))
+            layer.post_attention_layernorm.weight.copy_(t(w.mlp_norm))
+            layer.mlp.gate_proj.weight.copy_(t(wgu[:cfg.inter]))
+            layer.mlp.up_proj.weight.copy_(t(wgu[cfg.inter:]))
+            layer.mlp.down_proj.weight.copy_(t(w.wd.full()))
+        cos, sin = MO.rope_cos_sin(L + np.arange(B), cfg.d, cfg.rope_theta)
+        model.rotary_emb = _FixedRope(t(np.concatenate([cos, cos], -1))[None],
+                                      t(np.concatenate([sin, sin], -1))[None])
+        cache = DynamicCache(config=hc)
+        for l in range(cfg.n_layers):
+            if L:
+                cache.update(t(prefix[l][0].transpose(1, 0, 2))[None],
+                             t(prefix[l][1].transpose(1, 0, 2))[None], l)
+        ids = torch.tensor(np.where(tok == O.MASK, cfg.mask_id, tok))[None]
+        mask = torch.zeros(1, 1, B, L + B, dtype=torch.float64)   # every key visible
+        ref = model(input_ids=ids, attention_mask={"full_attention": mask},
+                    position_ids=torch.tensor(L + np.arange(B))[None], past_key_values=cache,
+                    use_cache=True).last_hidden_state[0].numpy()
+    # transformers keeps the norms' statistics and the softmax in float32
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    # the masked positions took the mask token's row: with no prefix they only
+    # differ through their position
+    assert not np.allclose(got[1], got[4])
 
 
 def test_rope_angles_match_transformers():
