@@ -24,6 +24,13 @@
 //                 float32, P entering PV as a bf16 hi + lo pair so the
 //                 probabilities keep ~16 significant bits.  Units may be split
 //                 over workgroups; k_attn_combine merges the splits.
+//   k_attn_wide   bf16, d = 128, prefixes of 4096 keys and more.  128 query
+//                 rows per workgroup and eight compute waves (two per SIMD)
+//                 that issue the buffer-to-LDS loads themselves into a
+//                 four-stage ring; each wave pipelines its units into matrix
+//                 phases (scores of the next unit, P V of this one) and
+//                 vector phases (softmax), and the two waves of a SIMD run one
+//                 phase apart.
 //   k_attn_plain  any dtype / d <= 256: one wave per query row, keys in
 //                 chunks of 1024 with online softmax, float32 throughout.
 #include <type_traits>
@@ -369,6 +376,381 @@ k_attn_dma(int L, int B, int Hq, int Hkv, int nb_max, int splits,
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path, 128-row workgroups of eight compute waves (long prefixes)
+// ---------------------------------------------------------------------------
+//
+// k_attn_wide: eight waves, all of them computing and each issuing an equal
+// share of every unit's buffer-to-LDS loads into a four-stage ring.  Wave w
+// owns 32 query rows (w & 3) and one 32-key half of every unit (w >> 2).
+// Per unit and wave: S^T = K Q^T as one chain of 8 MFMAs, the probabilities
+// split into a truncated bf16 high part and the bf16-rounded exact
+// remainder, O^T += V^T P^T as 16 MFMAs.  Each wave pipelines its units into
+// matrix phases (the next unit's scores and this unit's products) and vector
+// phases (the next unit's softmax), and waves 4..7 run one phase behind
+// waves 0..3 -- waves w and w + 4 share a SIMD, so while one issues MFMAs the
+// other runs its softmax.  Measured against k_attn_dma (prefix 4096, 9
+// branches of block 64, 28 q-heads over 4 KV heads): 73.7 against 84.8 us;
+// the per-phase timing shows the matrix phase at about twice its MFMA time
+// and the vector phase slowed about twofold by the other wave's MFMAs, so
+// the two waves' work still overlaps only in part.
+
+constexpr int kWRows = 128;
+constexpr int kWThreads = 512;
+constexpr int kWStages = 4;       // LDS ring depth (units of 32 KB)
+constexpr int kWDmaPerUnit = 4;   // 16-byte LDS loads per wave per unit
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0)
+template <int VM>
+__device__ __forceinline__ void attn_wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void attn_raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(kWThreads)
+k_attn_wide(int L, int B, int Hq, int Hkv, int nb_max, int row_groups, int splits,
+            const int32_t* __restrict__ nb_ptr, const unsigned short* __restrict__ Kp,
+            const unsigned short* __restrict__ Vp, const unsigned short* __restrict__ Qb,
+            const unsigned short* __restrict__ Kb, const unsigned short* __restrict__ Vb,
+            unsigned short* __restrict__ H, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kWStages * 2 * kAHalf];
+  // Consecutive workgroup ids go to consecutive XCDs (eight of them): id i
+  // takes slot (i % 8) * (grid / 8) + i / 8 of the (KV head, split, row
+  // group) order, so each XCD works through a contiguous stretch of it --
+  // one or two KV heads, whose prefix its own L2 then serves.
+  const int per = gridDim.x >> 3;
+  const int slot = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (slot >= row_groups * splits * Hkv) return;
+  const int rg = slot % row_groups;
+  const int split = (slot / row_groups) % splits;
+  const int g = slot / (row_groups * splits);
+  const int G = Hq / Hkv;
+  const int RB = B * G;
+  const int nb = __builtin_amdgcn_readfirstlane(min(max(*nb_ptr, 0), nb_max));
+  const int R = nb * RB;
+  const int r0 = rg * kWRows;
+  if (r0 >= R) return;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  const int nbp = (L + kAUnitKeys - 1) / kAUnitKeys;
+  const int obp = (B + kAUnitKeys - 1) / kAUnitKeys;
+  const int b_lo = r0 / RB;
+  const int b_hi = (min(r0 + kWRows, R) - 1) / RB;
+  const int units = nbp + (b_hi - b_lo + 1) * obp;
+  const int u_lo = static_cast<int>(static_cast<long long>(split) * units / splits);
+  const int u_hi = static_cast<int>(static_cast<long long>(split + 1) * units / splits);
+  const int n = u_hi - u_lo;
+
+  // ---- loads: wave w moves key rows 4(w + 8p) .. +3, p = 0, 1, of K and V ----
+  const int kq = lane >> 4;
+  const int ps = lane & 15;
+  const __amdgpu_buffer_rsrc_t kpr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(Kp), 0, L * Hkv * kARowBytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vpr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(Vp), 0, L * Hkv * kARowBytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t kbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(Kb), 0, nb_max * B * Hkv * kARowBytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(Vb), 0, nb_max * B * Hkv * kARowBytes, 0x00020000);
+  // unit number i -> stage i % kWStages; past the end the last unit is loaded
+  // again, so every iteration sees the same number of loads in flight
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    unsigned char* st = smem + (i % kWStages) * 2 * kAHalf;
+    const int u = u_lo + min(i, n - 1);
+    const bool own = u >= nbp;
+    const int v = u - nbp;
+    const int kn = own ? min(kAUnitKeys, B - (v % obp) * kAUnitKeys)
+                       : min(kAUnitKeys, L - u * kAUnitKeys);
+    const int key0 = own ? (b_lo + v / obp) * B + (v % obp) * kAUnitKeys : u * kAUnitKeys;
+    const __amdgpu_buffer_rsrc_t kr_ = own ? kbr : kpr;
+    const __amdgpu_buffer_rsrc_t vr_ = own ? vbr : vpr;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kr = 4 * (w + 8 * p) + kq;
+      const int key = key0 + min(kr, kn - 1);
+      const int off = ((key * Hkv + g) * kAD + ((ps ^ aswz(kr)) << 3)) * 2;
+      unsigned char* dk = st + (w + 8 * p) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_, LOPA_LDS_PTR(dk), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr_, LOPA_LDS_PTR(dk + kAHalf), 16, off, 0, 0, 0);
+    }
+  };
+
+  // ---- the wave's rows: tile rt, keys 32 kh .. +31 of every unit ----
+  const int rt = w & 3, kh = w >> 2;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  const int grow = r0 + 32 * rt + ln;
+  const int row = min(grow, R - 1);
+  const int rbr = row / RB;
+  const int rem = row - rbr * RB;
+  const int qoff = ((rbr * B + rem / G) * Hq + g * G + rem % G) * kAD;
+  u16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const u16x8*>(Qb + qoff + 16 * s + 8 * lh);
+
+  const float scale2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o[u] = f32x16{};
+
+  // transposed V reads: lane (q = lane/16, i = lane%16) supplies the address
+  // of key 16 tp + 4 hh + 8(q/2) + i/4 of the wave's half, dims 32 u + 16(q%2)
+  // + 4(i%4) .. +4.  The row swizzle aswz(key) has high bits i/4 (the same for
+  // every read of a lane) and low bits that depend on hh only, so a read's
+  // byte offset is vbase[hh] + ((64 u) ^ a64) + 4096 tp.
+  const int tq = lane >> 4, ti = lane & 15;
+  const int vkey = 8 * (tq >> 1) + (ti >> 2);
+  const int vdim = 16 * (tq & 1) + 4 * (ti & 3);
+  const int a64 = (ti >> 2) << 6;
+  int vbase[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int key = 32 * kh + 4 * hh + vkey;
+    vbase[hh] = key * kARowBytes + (((vdim >> 3) ^ (aswz(key) & 3)) << 4) + ((vdim & 7) << 1);
+  }
+  const int kr_s = 32 * kh + kperm(ln);
+  const int sw_s = aswz(kr_s);
+
+  // S^T = K Q^T of unit i over the wave's 32 keys: one chain of 8 MFMAs
+  auto s_part = [&](int i) __attribute__((always_inline)) {
+    const unsigned char* Ks = smem + (i % kWStages) * 2 * kAHalf;
+    u16x8 kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      kf[s] = *reinterpret_cast<const u16x8*>(Ks + kr_s * kARowBytes + (((2 * s + lh) ^ sw_s) << 4));
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]),
+                                                   __builtin_bit_cast(bf16x8, qf[s]), sc, 0, 0, 0);
+    return sc;
+  };
+  // O^T += V^T P^T of unit i: 16 MFMAs, the same accumulator's two products
+  // 4 apart; each 16-key step's V^T fragments are read just before it
+  auto pv_part = [&](int i, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2])
+      __attribute__((always_inline)) {
+    const unsigned char* Vs = smem + (i % kWStages) * 2 * kAHalf + kAHalf;
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      bf16x4 va[4][2];
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int byte = vbase[hh] + ((64 * u2) ^ a64) + 16 * kARowBytes * tp;
+          va[u2][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+                  reinterpret_cast<uintptr_t>(Vs + byte)));
+        }
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const bf16x8 vf = __builtin_shufflevector(va[u2][0], va[u2][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, hl ? plo[tp] : phi[tp], o[u2], 0,
+                                                          0, 0);
+        }
+    }
+  };
+  // P^T operands of scores sc under exponent reference m: the bf16 high part
+  // (truncated) and the bf16-rounded exact remainder; returns their sum
+  auto probs = [&](const float (&scm)[16], float m, bf16x8 (&phi)[2], bf16x8 (&plo)[2])
+      __attribute__((always_inline)) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      u16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(scm[8 * tp + e], scale2, -m));
+        lsum += p;
+        const unsigned pb = __float_as_uint(p);
+        h[e] = static_cast<unsigned short>(pb >> 16);
+        plo[tp][e] = static_cast<bf16>(p - __uint_as_float(pb & 0xffff0000u));
+      }
+      phi[tp] = __builtin_bit_cast(bf16x8, h);
+    }
+    return lsum;
+  };
+  // block maximum of the scores (log2 units), both halves of the wave
+  auto block_max = [&](const float (&scm)[16]) __attribute__((always_inline)) {
+    float mx = scm[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, scm[r]);
+    return fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale2;
+  };
+  // Softmax of unit i's scores sc into the P^T operands, with masking for
+  // partial and own-block units; the exponent reference of a row moves only
+  // when a block maximum exceeds it by more than 8 (log2 units), rescaling O
+  // and l (O / l is the same for any reference), so p <= 2^8.
+  auto soft = [&](int i, const f32x16& sc, bf16x8 (&phi)[2], bf16x8 (&plo)[2])
+      __attribute__((always_inline)) {
+    const int u = u_lo + i;
+    float scm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) scm[r] = sc[r];
+    if (u >= L / kAUnitKeys) {   // not a full prefix unit
+      const bool own = u >= nbp;
+      const int v = u - nbp;
+      const int kn = own ? min(kAUnitKeys, B - (v % obp) * kAUnitKeys)
+                         : min(kAUnitKeys, L - u * kAUnitKeys);
+      const bool see = !own || rbr == b_lo + v / obp;
+      // sc[r] = raw score of key 32kh + 16(r/8) + 8lh + r%8
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kh + 16 * (r >> 3) + 8 * lh + (r & 7);
+        if (!(see && key < kn)) scm[r] = -INFINITY;
+      }
+    }
+    const float bmax = block_max(scm);
+    const bool grow_ref = bmax > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow_ref)) {
+      const float m_new = grow_ref ? bmax : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 from -inf
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) o[u2] *= alpha;
+    }
+    // a row that has seen no key yet keeps m_ref = -inf and all p = 0
+    l_run += probs(scm, m_ref == -INFINITY ? 0.f : m_ref, phi, plo);
+  };
+
+  // Schedule.  A wave takes each unit u through S_u (scores), soft_u and
+  // PV_u, pipelined into phases: M(-1) = S_0, V(-1) = soft_0, then
+  // M(j) = {S_(j+1), PV_j} and V(j) = soft_(j+1) for j < n - 1, and last
+  // M(n-1) = PV_(n-1): 2n + 1 phases of matrix (M) or vector (V) work.
+  // Waves 0-3 run phase p in slot p, waves 4-7 in slot p + 1, and every slot
+  // ends at a workgroup barrier: each SIMD holds one wave of each group, so
+  // one wave's softmax runs while the other's MFMAs do.
+  // Ring: unit v is loaded at the start of slot 2v - 4 (units 0, 1 before
+  // slot 0) into stage v % 4, whose previous unit v - 4 was last read in slot
+  // 2v - 5; unit u is first read in slot 2u, and at the end of slot 2u - 1
+  // each wave waits for its loads of unit u (those of u + 1 may be in flight).
+  f32x16 sc = f32x16{};
+  bf16x8 phi[2], plo[2];
+  // end of slot s: this wave's loads of unit (s + 1) / 2 have landed when s
+  // is odd; then the workgroup barrier
+  auto end_slot = [&](bool odd) __attribute__((always_inline)) {
+    if (odd) attn_wait_vm_lgkm0<kWDmaPerUnit>();
+    else attn_wait_vm_lgkm0<2 * kWDmaPerUnit>();
+    attn_raw_barrier();
+  };
+  if (n > 0) {
+    issue(0);
+    issue(1);
+    attn_wait_vm_lgkm0<kWDmaPerUnit>();
+    attn_raw_barrier();
+    if (w < 4) {
+      // phase p in slot p; slot 2n + 1 idle
+      issue(2);
+      sc = s_part(0);                       // slot 0: S_0
+      end_slot(false);
+      for (int j = 0; j + 1 < n; ++j) {
+        soft(j, sc, phi, plo);              // slot 2j + 1: soft_j
+        end_slot(true);
+        issue(j + 3);                       // slot 2j + 2: S_(j+1), PV_j
+        sc = s_part(j + 1);
+        pv_part(j, phi, plo);
+        end_slot(false);
+      }
+      soft(n - 1, sc, phi, plo);            // slot 2n - 1
+      end_slot(true);
+      issue(n + 2);                         // slot 2n: PV_(n-1)
+      pv_part(n - 1, phi, plo);
+      end_slot(false);
+    } else {
+      // phase p in slot p + 1; slot 0 idle
+      issue(2);
+      end_slot(false);
+      sc = s_part(0);                       // slot 1: S_0
+      end_slot(true);
+      for (int j = 0; j + 1 < n; ++j) {
+        issue(j + 3);                       // slot 2j + 2: soft_j
+        soft(j, sc, phi, plo);
+        end_slot(false);
+        sc = s_part(j + 1);                 // slot 2j + 3: S_(j+1), PV_j
+        pv_part(j, phi, plo);
+        end_slot(true);
+      }
+      issue(n + 2);                         // slot 2n: soft_(n-1)
+      soft(n - 1, sc, phi, plo);
+      end_slot(false);
+      pv_part(n - 1, phi, plo);             // slot 2n + 1: PV_(n-1)
+    }
+  }
+  attn_wait_vm_lgkm0<0>();   // no load may still target the ring
+  attn_raw_barrier();
+
+  // ---- merge of the two key halves of each row tile, through the ring ----
+  float* xo = reinterpret_cast<float*>(smem) + rt * (64 * 64);             // [u2][r][lane]
+  float* xm = reinterpret_cast<float*>(smem) + 4 * (64 * 64) + rt * 128;   // m, then l
+  if (kh == 1) {
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(16 * u2 + r) * 64 + lane] = o[u2][r];
+    xm[lane] = m_ref;
+    xm[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float M = fmaxf(m_ref, m1);
+    const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[u2][r] = o[u2][r] * a0 + xo[(16 * u2 + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_ref = M;
+  }
+
+  // ---- output: o[u][r] = O[row][dim 32u + 8(r/4) + 4lh + r%4] ----
+  if (grow >= R) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (splits == 1) {
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const unsigned lo = f32_to_bf16_bits(o[u2][4 * a] * inv) |
+                            (static_cast<unsigned>(f32_to_bf16_bits(o[u2][4 * a + 1] * inv)) << 16);
+        const unsigned hi = f32_to_bf16_bits(o[u2][4 * a + 2] * inv) |
+                            (static_cast<unsigned>(f32_to_bf16_bits(o[u2][4 * a + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(H + qoff + 32 * u2 + 8 * a + 4 * lh) = make_uint2(lo, hi);
+      }
+  } else {
+    const size_t rmax = static_cast<size_t>(nb_max) * RB;
+    const size_t prow = (static_cast<size_t>(split) * Hkv + g) * rmax + grow;
+    float* po = part + prow * kAD;
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(po + 32 * u2 + 8 * a + 4 * lh) =
+            f32x4{o[u2][4 * a], o[u2][4 * a + 1], o[u2][4 * a + 2], o[u2][4 * a + 3]};
+    if (lh == 0) {
+      float* pm = part + static_cast<size_t>(splits) * Hkv * rmax * kAD;
+      pm[prow] = m_ref;
+      pm[static_cast<size_t>(splits) * Hkv * rmax + prow] = l_tot;
+    }
+  }
+}
+
 // Merge of the splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // rounded to bf16.  One wave per row (2 dims per lane); every split's loads
 // are issued before any is used, so the merge costs one memory round trip.
@@ -500,14 +882,23 @@ extern "C" int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const voi
     // byte offsets
     if (static_cast<long long>(dims->L) * dims->Hkv * dims->d * 2 >= (1LL << 31))
       return LOPA_ERR_UNSUPPORTED;
-    const dim3 grid(p.row_groups, dims->Hkv, p.splits);
-    hipLaunchKernelGGL(k_attn_dma, grid, dim3(512), 0, stream, dims->L, dims->B, dims->Hq,
-                       dims->Hkv, nb_max, p.splits, nb, static_cast<const unsigned short*>(Kp),
-                       static_cast<const unsigned short*>(Vp),
-                       static_cast<const unsigned short*>(Qb),
-                       static_cast<const unsigned short*>(Kb),
-                       static_cast<const unsigned short*>(Vb), static_cast<unsigned short*>(H),
-                       static_cast<float*>(ws));
+    const auto* kp = static_cast<const unsigned short*>(Kp);
+    const auto* vp = static_cast<const unsigned short*>(Vp);
+    const auto* qb = static_cast<const unsigned short*>(Qb);
+    const auto* kb = static_cast<const unsigned short*>(Kb);
+    const auto* vb = static_cast<const unsigned short*>(Vb);
+    if (p.wide) {
+      const int wgs = p.row_groups * dims->Hkv * p.splits;
+      hipLaunchKernelGGL(k_attn_wide, dim3((wgs + 7) / 8 * 8), dim3(kWThreads), 0, stream,
+                         dims->L, dims->B, dims->Hq, dims->Hkv, nb_max, p.row_groups, p.splits,
+                         nb, kp, vp, qb, kb, vb, static_cast<unsigned short*>(H),
+                         static_cast<float*>(ws));
+    } else {
+      const dim3 grid(p.row_groups, dims->Hkv, p.splits);
+      hipLaunchKernelGGL(k_attn_dma, grid, dim3(512), 0, stream, dims->L, dims->B, dims->Hq,
+                         dims->Hkv, nb_max, p.splits, nb, kp, vp, qb, kb, vb,
+                         static_cast<unsigned short*>(H), static_cast<float*>(ws));
+    }
     LOPA_LAUNCH_CHECK();
     if (p.splits > 1) {
       const int rows = nb_max * dims->B * (dims->Hq / dims->Hkv);

@@ -112,7 +112,9 @@ def test_workspace_size_and_shortfall():
     assert need == 3 * 4 * (5 * 32 * 7) * 130 * 4
     # 9 branches: 128 workgroups leave room for 2 splits, which would not pay
     assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 20
-    assert lopa.workspace_bytes(_dims(L=4096, B=64, k_max=8)) == 9 * 64 * 256 * 20
+    # prefix 4096 takes the 128-row kernel: 32 row groups x 4 heads = 128
+    # workgroups -> 2 splits (33 units + the merge's 8 < 65)
+    assert lopa.workspace_bytes(_dims(L=4096, B=64, k_max=8)) == 2 * 4 * (9 * 64 * 7) * 130 * 4
     # prefix 2048: 33 units over 32 row groups x 4 heads = 128 workgroups ->
     # 2 splits (17 + 5 < 33)
     split = _dims(L=2048, k_max=8)

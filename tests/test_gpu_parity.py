@@ -149,6 +149,14 @@ ATTN_CASES = [
     # a full 64-key own block; 32-row tiles straddling branches (B*G = 140)
     ("bf16-mfma-B64", dict(dtype="bf16", L=200, B=64, m=8, Hq=28, Hkv=4, d=128, k=2), 3),
     ("bf16-mfma-B20-G7", dict(dtype="bf16", L=64, B=20, m=8, Hq=28, Hkv=4, d=128, k=3), 4),
+    # prefixes of 4096 keys and more: the 128-row kernel.  192 rows over 2 row
+    # groups (the second half empty), branches of 64 rows, 16 splits
+    ("bf16-wide-16splits", dict(dtype="bf16", L=4133, B=16, m=8, Hq=4, Hkv=1, d=128, k=2), 3),
+    # G = 7: 128-row workgroups straddle branches (B*G = 140); dead slots
+    ("bf16-wide-B20-G7", dict(dtype="bf16", L=4100, B=20, m=8, Hq=28, Hkv=4, d=128, k=3), 3),
+    # a full 64-key own block, 2 splits
+    ("bf16-wide-B64", dict(dtype="bf16", L=4096, B=64, m=8, Hq=14, Hkv=2, d=128, k=4), 5),
+    ("bf16-wide-nb1", dict(dtype="bf16", L=5000, B=16, m=8, Hq=8, Hkv=2, d=128, k=3), 1),
 ]
 
 
@@ -187,6 +195,45 @@ def test_gpu_attn_ragged_last_unit(kn):
     torch.cuda.synchronize()
     Hx = O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv)
     assert_h_close(act_to_f64(buf.H)[:nb], Hx[:nb], cfg.dtype, f"kn={kn}")
+
+
+@pytest.mark.parametrize("kn", [1, 31, 32, 33, 63])
+def test_gpu_attn_wide_ragged_last_unit(kn):
+    """The 128-row kernel with the prefix ending inside a 64-key unit."""
+    ov = dict(dtype="bf16", L=4096 + kn, B=16, m=8, Hq=4, Hkv=1, d=128, k=2)
+    inp = synth.make_inputs(synth.TINY, with_weight=False, **ov)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    x = device_inputs(inp)
+    buf = StepBuffers(dims)
+    nb = dims.nb_max
+    lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"],
+                          to_device(np.array([nb], np.int32)), buf.H, buf.ws)
+    torch.cuda.synchronize()
+    Hx = O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv)
+    assert_h_close(act_to_f64(buf.H)[:nb], Hx[:nb], cfg.dtype, f"kn={kn}")
+
+
+@pytest.mark.parametrize("L", [1500, 4100])
+def test_gpu_attn_scores_outgrow_the_first_units(L):
+    """Keys in the second half of the prefix score up to ~40 (log2 units)
+    above the first ones, so a row's exponent reference moves many times and
+    O and l are rescaled (both attention kernels)."""
+    ov = dict(dtype="bf16", L=L, B=16, m=8, Hq=8, Hkv=2, d=128, k=3)
+    inp = synth.make_inputs(synth.TINY, with_weight=False, **ov)
+    K = O.bf16_to_f64(inp.Kp)
+    K[L // 2:] *= 1.0 + 11.0 * np.linspace(0.0, 1.0, L - L // 2)[:, None, None]
+    inp.Kp = synth.f32_to_bf16_bits(K.astype(np.float32)).reshape(inp.Kp.shape)
+    cfg = inp.cfg
+    dims = dims_of(cfg)
+    x = device_inputs(inp)
+    buf = StepBuffers(dims)
+    nb = dims.nb_max
+    lopa.lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"],
+                          to_device(np.array([nb], np.int32)), buf.H, buf.ws)
+    torch.cuda.synchronize()
+    Hx = O.branch_attn(inp.Kp, inp.Vp, inp.Qb, inp.Kb, inp.Vb, nb, cfg.Hq, cfg.Hkv)
+    assert_h_close(act_to_f64(buf.H)[:nb], Hx[:nb], cfg.dtype, f"L={L}")
 
 
 # ---------------------------------------------------------------------------
