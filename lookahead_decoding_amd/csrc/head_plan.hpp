@@ -78,9 +78,13 @@ __host__ __device__ inline HeadGroups head_groups(int M) {
 // same number of MFMAs.  tw: weight tiles per pass (8 while the LDS allows
 // it, else 4).  It serves the row-tile counts where it measured faster than
 // the narrow kernel (k_lmhead_mfma) in a same-box comparison at every count
-// from 5 to 32 tiles at the 7B shapes: 5, 6, 9, 13, 17 and 18 tiles (by 12,
-// 3, 8, 2, 4 and 2 %); the narrow kernel serves every other count.
-constexpr int kHeadNarrowRows = 128;
+// from 5 to 32 tiles at the 7B shapes: 6, 9, 13, 17 and 18 tiles (by 3, 8,
+// 2, 4 and 2 %); the narrow kernel serves every other count.  At 5 tiles it
+// measured 12 % faster as well, but the row count lives on the device, so a
+// call that may reach the wide kernel launches both and the idle one costs
+// about 5 us: a call of at most 5 tiles (block 32, 5 branches: m_max = 160)
+// launches the narrow kernel alone.
+constexpr int kWideMinTiles = 6;
 constexpr int kWideMaxTiles = 13;
 
 struct WideGroups {
@@ -96,7 +100,7 @@ __host__ __device__ inline WideGroups wide_groups(int M) {
 
 __host__ __device__ inline bool wide_takes(int M) {
   const int t = (M + 31) / 32;
-  return t == 5 || t == 6 || t == 9 || t == 13 || t == 17 || t == 18;
+  return t == 6 || t == 9 || t == 13 || t == 17 || t == 18;
 }
 
 // Vocabulary parts per row of whichever MFMA kernel serves M rows (wide:

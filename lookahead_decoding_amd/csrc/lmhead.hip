@@ -1043,7 +1043,6 @@ k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int h_bytes,
 #define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
                   ws_t, ws_z, smp
   switch (g.th) {   // the layouts wide_takes() can reach
-    case 5: wide_body<8, 1, 1, MODE>(LOPA_ARGS); break;
     case 6: wide_body<8, 1, 2, MODE>(LOPA_ARGS); break;
     case 9: wide_body<4, 2, 1, MODE>(LOPA_ARGS); break;
     default: wide_body<4, 3, 1, MODE>(LOPA_ARGS); break;
@@ -1164,12 +1163,12 @@ k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
 }  // namespace lopa
 
 // The wide kernel is launched beside the narrow one when the device-side row
-// count may reach one it serves (more than kHeadNarrowRows rows; confidence
-// and entropy modes, no full logits requested).
+// count may reach one it serves (m_max of kWideMinTiles 32-row tiles or more;
+// confidence and entropy modes, no full logits requested).
 template <int MODE>
 static bool wide_serves(const lopa::HeadPlan& p, int hidden, const float* logits_out) {
   (void)hidden;
-  return MODE != lopa::kModeSample && p.mfma && p.m_max > lopa::kHeadNarrowRows &&
+  return MODE != lopa::kModeSample && p.mfma && (p.m_max + 31) / 32 >= lopa::kWideMinTiles &&
          logits_out == nullptr;
 }
 

@@ -296,17 +296,18 @@ def test_gpu_lmhead(name, ov, _):
     np.testing.assert_allclose(lg, ref.logits, rtol=1e-5, atol=1e-5 * np.abs(ref.logits).max())
 
 
-# More than 128 rows, without full logits: the wide kernel (four waves,
-# register tiles of q owned row tiles plus a share of the r remaining ones)
-# where it serves the row-tile count (5, 6, 9, 13, 17, 18), the narrow one
-# elsewhere.  Row groups of th = 4q + r tiles, 8 weight tiles per pass up to 7
-# row tiles, 4 from 8; vocabulary parts with empty parts (V < 4096), a last
+# Without full logits, m_max of 6 row tiles or more: the wide kernel (four
+# waves, register tiles of q owned row tiles plus a share of the r remaining
+# ones) where it serves the row-tile count (6, 9, 13, 17, 18), the narrow one
+# elsewhere (and alone when m_max is at most 5 tiles).  Row groups of
+# th = 4q + r tiles, 8 weight tiles per pass up to 7 row tiles, 4 from 8; vocabulary parts with empty parts (V < 4096), a last
 # pass of 1 .. all live weight tiles, a vocabulary size that is not a
 # multiple of 16, and 2 and 3 row groups.  Rows: every masked position of
 # every branch slot.
 WIDE_CASES = [
     # name, overrides (M = (k + 1) m)
-    ("th5-empty-parts", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=3000, B=32, m=30, k=4)),
+    ("tiles5-narrow-alone", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=3000, B=32, m=30, k=4)),
+    ("th6-empty-parts", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=3000, B=48, m=45, k=3)),
     ("th6-tw8", dict(dtype="bf16", Hq=2, Hkv=2, d=64, V=9000, B=60, m=60, k=2)),
     ("th6-tw8-last-5", dict(dtype="bf16", Hq=2, Hkv=2, d=64, V=37100, B=60, m=60, k=2)),
     ("th7-tw8-two-passes", dict(dtype="bf16", Hq=1, Hkv=1, d=128, V=65636, B=56, m=56, k=3)),
