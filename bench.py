@@ -30,23 +30,39 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
-# HBM bytes per lopa_lmhead_conf call (k_lmhead_mfma + k_lmhead_merge) from two
-# rocprofv3 --pmc runs of this script: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB
-# per dispatch; the factors are what the same counters read for a 1 GiB device
-# copy).  Keyed by workload and by a hash of the kernel sources the counters
-# were taken on: after any change to those sources the figure is not reported.
+# HBM bytes per lopa_lmhead_conf call (k_lmhead_mfma + k_lmhead_wide +
+# k_lmhead_merge) and per lopa_branch_attn call (k_attn_dma or k_attn_wide +
+# k_attn_combine) from two rocprofv3 --pmc runs of this script: FETCH_SIZE x
+# 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are what the same
+# counters read for a 1 GiB device copy).  Keyed by workload and by a hash of
+# the kernel sources the counters were taken on: after any change to those
+# sources the figure is not reported.
 HEAD_SOURCES = ("lmhead.hip", "head_plan.hpp", "stream_tile.hpp", "lopa_common.hpp")
+ATTN_SOURCES = ("attn.hip", "attn_plan.hpp", "lopa_common.hpp")
 HEAD_TRAFFIC = {
-    "7b-bf16-L512-B32-m24-k4": ("39e07edd3489ba56", 1104675136),
+    "7b-bf16-L512-B32-m24-k4": ("594a44e1074e839a", 1104571012),
+    "7b-bf16-L2048-B32-m28-k8": ("594a44e1074e839a", 1111050834),
+    "7b-bf16-L1024-B32-m24-k15": ("594a44e1074e839a", 1115839516),
+    "7b-bf16-L4096-B64-m48-k8": ("594a44e1074e839a", 1158992839),
+}
+ATTN_TRAFFIC = {
+    "7b-bf16-L512-B32-m24-k4": ("b83e9d0f5e96b081", 26936320),
+    "7b-bf16-L2048-B32-m28-k8": ("b83e9d0f5e96b081", 58028288),
+    "7b-bf16-L1024-B32-m24-k15": ("b83e9d0f5e96b081", 28515328),
+    "7b-bf16-L4096-B64-m48-k8": ("b83e9d0f5e96b081", 57835008),
 }
 
 
-def head_source_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in HEAD_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "lookahead_decoding_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def head_source_hash() -> str:
+    return source_hash(HEAD_SOURCES)
 
 
 def parse():
@@ -457,7 +473,7 @@ def measure_workload(name: str, args, headline: bool) -> tuple[dict, dict]:
         "t_k_over_t_k0": None if ms0 is None else round(ms / ms0, 4),
         "call_us": calls,
         "roofline": head_roofline(cfg, alg, head_us),
-        "attn_roofline": attn_roofline(alg, float(call_us[1])),
+        "attn_roofline": attn_roofline(cfg, alg, float(call_us[1])),
     }
     ctx = dict(inp=inp, cfg=cfg, dims=dims, x=x, buf=buf)
     return rec, ctx
@@ -474,7 +490,7 @@ def head_roofline(cfg, alg, head_us: float) -> dict:
     # pass the bf16 ridge and make it MFMA-bound)
     mfma_bound = (alg["head_flops"] / (BF16_PEAK_TFLOPS * 1e12) >
                   alg["head_bytes"] / (HBM_PEAK_GBS * 1e9))
-    kern = "lopa_lmhead_conf (k_lmhead_mfma + k_lmhead_merge)"
+    kern = "lopa_lmhead_conf (k_lmhead_mfma or k_lmhead_wide, + k_lmhead_merge)"
     if mfma_bound:
         return {"kernel": kern, "bound": "mfma", "achieved": round(tflops, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -489,13 +505,15 @@ def head_roofline(cfg, alg, head_us: float) -> dict:
             "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
-def attn_roofline(alg, attn_us: float) -> dict:
+def attn_roofline(cfg, alg, attn_us: float) -> dict:
     """Attention call (event-timed, so it includes one event gap of a few
     microseconds): its flops against the bf16 MFMA peak and its algorithmic
-    bytes against HBM."""
+    bytes against HBM; traffic as for the LM head."""
+    tr = ATTN_TRAFFIC.get(cfg.name)
+    traffic = tr[1] if tr is not None and tr[0] == source_hash(ATTN_SOURCES) else None
     tflops = alg["attn_flops"] / (attn_us * 1e-6) / 1e12
     gbs = alg["attn_bytes"] / (attn_us * 1e-6) / 1e9
-    return {"call_us": round(attn_us, 2), "tflops": round(tflops, 1),
+    return {"call_us": round(attn_us, 2), "tflops": round(tflops, 1), "traffic": traffic,
             "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4), "gbs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_flops_per_call": alg["attn_flops"],
