@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-model", action="store_true",
                     help="skip the step with the 28-layer model forward")
+    ap.add_argument("--model-no-decode", action="store_true",
+                    help="time the model step only, not the block decoded with the model")
     ap.add_argument("--model-steps", type=int, default=30)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run 3 device copies of 1 GiB (a reference for byte counters)")
@@ -154,7 +156,7 @@ def model_bytes(dims, md) -> dict:
                 flops=2.0 * M * (md.n_layers * layer_w / e))
 
 
-def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
+def model_measure(cfg, inp, steps: int, warmup: int, decode: bool = True) -> dict:
     """A verification step with the 28-layer Qwen2.5/Dream-7B-shaped forward
     (synthetic weights): build -> lopa_branch_forward -> lopa_lmhead_conf
     (the model's LM head) -> select; and the same with one branch (k_max 0)
@@ -169,6 +171,7 @@ def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
            "weights_gb": None}
 
     def run(k_max: int, k: int) -> dict:
+        progress(f"28-layer model step, k_max {k_max}")
         dims = dims_of(cfg)
         dims.k_max = k_max
         model = Model(dims, md, seed=0x7B00 + inp.seed)
@@ -220,7 +223,20 @@ def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
         head_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         alg = model_bytes(dims, md)
         ach = alg["forward_bytes"] / (fwd_ms * 1e-3) / 1e9
+        res = {"k": k, "branches": int(buf.nb.item()), "rows": nbm * B,
+               "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 3),
+               "forward_ms": round(fwd_ms, 3), "lmhead_ms": round(head_ms, 3),
+               "forward_roofline": {"bound": "hbm", "achieved": round(ach, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                                    "algorithmic_bytes": alg["forward_bytes"],
+                                    "mfma_tflops": round(alg["flops"] / (fwd_ms * 1e-3) / 1e12, 1)}}
+        if not decode:
+            del model, buf, fb
+            torch.cuda.empty_cache()
+            return res
         # the block decoded with the model until nothing is masked
+        progress(f"28-layer model decode, k_max {k_max}")
         from lookahead_decoding_amd.model import ModelDecodeBuffers, model_decode_block
         m = len(masked)
         dbuf = ModelDecodeBuffers(dims, md)
@@ -235,17 +251,9 @@ def model_measure(cfg, inp, steps: int, warmup: int) -> dict:
             model_decode_block(model, dims, k, cfg.tau, tok, dbuf, dsteps)
         torch.cuda.synchronize()
         dms = (time.perf_counter() - t0) / 2 * 1e3
-        decode = {"masked": m, "steps": dsteps, "tpf": round(m / dsteps, 3),
-                  "ms_per_block": round(dms, 2), "decoded_tokens_per_s": round(m / (dms * 1e-3), 1)}
-        res = {"k": k, "branches": int(buf.nb.item()), "rows": nbm * B,
-               "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 3),
-               "forward_ms": round(fwd_ms, 3), "lmhead_ms": round(head_ms, 3),
-               "forward_roofline": {"bound": "hbm", "achieved": round(ach, 1),
-                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(ach / HBM_PEAK_GBS, 4),
-                                    "algorithmic_bytes": alg["forward_bytes"],
-                                    "mfma_tflops": round(alg["flops"] / (fwd_ms * 1e-3) / 1e12, 1)},
-               "decode": decode}
+        res["decode"] = {"masked": m, "steps": dsteps, "tpf": round(m / dsteps, 3),
+                         "ms_per_block": round(dms, 2),
+                         "decoded_tokens_per_s": round(m / (dms * 1e-3), 1)}
         del model, buf, fb, dbuf
         torch.cuda.empty_cache()
         return res
@@ -578,7 +586,8 @@ def main():
         }
     if not args.no_model and cfg.dtype == "bf16":
         progress("28-layer model step")
-        out["model_step"] = model_measure(cfg, inp, args.model_steps, 5)
+        out["model_step"] = model_measure(cfg, inp, args.model_steps, 5,
+                                          decode=not args.model_no_decode)
     del ctx, x
     torch.cuda.empty_cache()
     # every 7B workload, each timed like the headline (its own inputs)
