@@ -30,6 +30,7 @@
 //                   per vocabulary entry, FMA dot products.
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "lopa_common.hpp"
 #include "head_plan.hpp"
@@ -42,6 +43,16 @@ namespace lopa {
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // What the LM head folds per row: the confidence and argmax; also the
 // entropy term; or, for temperature sampling, the scaled-logit softmax and a
@@ -530,20 +541,25 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
 // issues its share of the loads that fill the LDS rings (the weight: three
 // stages, two chunks in flight; the group's activation rows: two stages, one
 // chunk in flight, from L2), so no wave is spent on loading alone.  One
-// barrier per K chunk, taken in K step 2: fragments are read two steps
-// ahead, so by then the chunk's stages hold nothing still to be read, and
-// the two steps after it read the next chunk while their MFMAs run.  The
-// barrier waits for this wave's own loads of the next chunk (vmcnt) and its
-// LDS reads (lgkmcnt), and neither it nor the compiler lets memory accesses
+// barrier per K chunk, taken in the chunk's last K step after its first few
+// MFMAs: by then this wave's reads of the chunk are done (they run one step
+// ahead), and the step's remaining MFMAs carry the loads into the freed
+// stages and the reads of the next chunk's first step.  With one wave per
+// SIMD nothing else hides a wait on LDS, so each MFMA is followed by one
+// read of the next step and the order is pinned with scheduling barriers;
+// the compiler's own order put reads next to their MFMAs and waited on them
+// (13 tiles: 460-475 against 490-500 us per call, same box).  The barrier
+// waits for this wave's own loads of the next chunk (vmcnt) and its LDS
+// reads (lgkmcnt), and neither it nor the compiler lets memory accesses
 // move across it (a __syncthreads() would wait for every load in flight).
 //
 // Measured against the narrow kernel (same box, 7B shapes): faster where
 // the narrow kernel changes layout (5, 6, 9, 17, 18 tiles) and by 2 % at 13,
-// slower elsewhere.  Alone, its MFMA work with the LDS fragment reads takes
-// 327 us at 13 tiles (1.38 PFLOP/s; back-to-back MFMA peaks at 2.0 PFLOP/s on
-// this part) and its loads with the reads 240-280 us, but together 495 us:
-// the LDS writes of the loads and the fragment reads compete, and the sum
-// moves about 50-65 bytes per clock through each CU's LDS in both kernels.
+// slower elsewhere (before the pinned order above).  Timing-only copies at 13
+// tiles: the MFMAs with their fragment reads alone take about 380 us, the
+// loads with the reads alone about 365 us; each CU restages all 416
+// activation rows from L2 for every 128 weight rows, so the L2-to-LDS
+// traffic (about 5 GB a call) is what the MFMAs have to hide.
 
 // Entry r of a lane's 16 (the 32x32 MFMA output layout) lies at vocabulary
 // vb + 4h + kTileOff(r).  The folds below compare these compile-time offsets
@@ -685,6 +701,26 @@ struct LoadCursor {
   }
 };
 
+// Fragment reads of one K step of the wide body (TW weight tiles, Q own and
+// R remaining activation tiles, TW / 4 weight tiles paired with each
+// remaining one), in the order the step's MFMAs -- own tiles t-major, then
+// the remaining pairs -- first use them: w0, h0, w1 .. w(TW-1),
+// h1 .. h(Q-1), then xw0, h(Q) .. h(Q+R-1), xw1 ...  kind 0: weight tile,
+// 1: activation tile, 2: paired weight tile.
+template <int TW, int Q, int R>
+struct WideOrder {
+  static constexpr int XP = TW / 4;
+  static constexpr int count = TW + Q + (R > 0 ? R + XP : 0);
+  static constexpr int kind(int i) {
+    return i == 0 ? 0 : i == 1 ? 1 : i <= TW ? 0 : i < TW + Q ? 1 : i == TW + Q ? 2
+         : i <= TW + Q + R ? 1 : 2;
+  }
+  static constexpr int index(int i) {
+    return i == 0 ? 0 : i == 1 ? 0 : i <= TW ? i - 1 : i < TW + Q ? i - TW : i == TW + Q ? 0
+         : i <= TW + Q + R ? Q + (i - TW - Q - 1) : i - TW - Q - R;
+  }
+};
+
 template <int TW, int Q, int R, int MODE>
 __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int part, int Mg,
                                           int row0, int h_bytes,
@@ -783,29 +819,28 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
       lhc.step(total, nch);
     };
 
-    // ---- fragments of K step j of the chunk in W stage sw / H stage sh
+    // ---- fragments of one K step: the weight tiles, the activation tiles
+    // this wave multiplies, and (R > 0) its weight tiles w + 4k paired with
+    // the remaining activation tiles.  They are read one at a time, in the
+    // order the step's MFMAs first use them (WideOrder).
     struct Frags {
       u16x8 w[TW], h[QR], xw[XP];
     };
-    auto read_frags = [&](int sw, int sh, int j, Frags& f) __attribute__((always_inline)) {
-      const unsigned char* wb = smem + sw * WBUF;
-      const unsigned char* hb = hbase + sh * HBUF;
+    using Ord = WideOrder<TW, Q, R>;
+    // read number k of K step j of the chunk in W stage sw / H stage sh
+    auto read_one = [&](auto k_c, int sw, int sh, int j, Frags& f) __attribute__((always_inline)) {
+      constexpr int k = decltype(k_c)::value;
+      constexpr int kind = Ord::kind(k), x = Ord::index(k);
       const int sl = 2 * j + lh;   // logical slot: K values 16j + 8lh .. +8
-#pragma unroll
-      for (int n = 0; n < TW; ++n) {
-        const int r = n * 32 + ln;
-        f.w[n] = *reinterpret_cast<const u16x8*>(wb + r * kRB + swz<kKC>(r, sl) * 16);
-      }
-#pragma unroll
-      for (int t = 0; t < QR; ++t)
-        f.h[t] = *reinterpret_cast<const u16x8*>(hb + hrow[t] * kRB + swz<kKC>(hrow[t], sl) * 16);
-      // weight tiles w + 4k: this wave's pairs with the remaining tiles
-      if constexpr (R > 0) {
-#pragma unroll
-        for (int k = 0; k < XP; ++k) {
-          const int r = (w + 4 * k) * 32 + ln;
-          f.xw[k] = *reinterpret_cast<const u16x8*>(wb + r * kRB + swz<kKC>(r, sl) * 16);
-        }
+      if constexpr (kind == 0) {
+        const int r = x * 32 + ln;
+        f.w[x] = *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
+      } else if constexpr (kind == 1) {
+        f.h[x] = *reinterpret_cast<const u16x8*>(hbase + sh * HBUF + hrow[x] * kRB +
+                                                 swz<kKC>(hrow[x], sl) * 16);
+      } else {
+        const int r = (w + 4 * x) * 32 + ln;
+        f.xw[x] = *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
       }
     };
 
@@ -822,23 +857,18 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     // NL: live weight tiles of the pass (the others are neither multiplied
     // nor folded); the remaining tiles' pairs always run (a pair past the
     // part reads zeros and its entries are dropped by the masked fold)
-    auto mfma_step = [&](auto nl_c, const Frags& f) __attribute__((always_inline)) {
-      constexpr int NL = decltype(nl_c)::value;
-#pragma unroll
-      for (int t = 0; t < Q; ++t)
-#pragma unroll
-        for (int n = 0; n < NL; ++n)
-          acc[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, f.h[t]), acc[t][n],
-              0, 0, 0);
-      if constexpr (R > 0) {
-#pragma unroll
-        for (int k = 0; k < XP; ++k)
-#pragma unroll
-          for (int t = 0; t < R; ++t)
-            accx[t][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, f.h[Q + t]),
-                accx[t][k], 0, 0, 0);
+    auto mfma_one = [&](auto nl_c, auto i_c, const Frags& f) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nl_c)::value, i = decltype(i_c)::value;
+      if constexpr (i < Q * NL) {
+        constexpr int t = i / NL, n = i % NL;
+        acc[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, f.h[t]), acc[t][n], 0,
+            0, 0);
+      } else {
+        constexpr int k = (i - Q * NL) / R, t = (i - Q * NL) % R;
+        accx[t][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, f.h[Q + t]),
+            accx[t][k], 0, 0, 0);
       }
     };
 
@@ -907,37 +937,76 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     raw_barrier();
     issue_h();
     issue_w();
-    // Fragments are read two K steps ahead: fr[j] holds step j of the chunk
-    // being computed (KS == 4 sets, indexed statically).
-    static_assert(KS == 4, "fragment ring");
-    Frags fr[KS];
+    // Fragments are read one K step ahead, one read after each MFMA, so a
+    // read has most of a step's MFMAs to land; the order is pinned with
+    // scheduling barriers (left to itself the compiler sinks the reads next
+    // to their MFMAs and waits on them there).
+    static_assert(KS == 4, "one chunk is four K steps");
+    constexpr int NR = Ord::count;
+    Frags f0, f1;
     int cw = 0, chs = 0;   // stages of the chunk being computed
-    read_frags(cw, chs, 0, fr[0]);
-    read_frags(cw, chs, 1, fr[1]);
-    // One chunk.  The barrier sits in step 2: by then every fragment of
-    // this chunk has been read (steps 2 and 3 at steps 0 and 1), so the
-    // chunk's stages are free for H(c + 2) and W(c + 3) once every wave has
-    // passed it; the two steps after it read the next chunk's first two
-    // steps while their MFMAs run.  (After the last chunk this re-loads the
-    // last chunk and reads stages that are not used: every wave takes the
-    // same steps.)
+    static_for<NR>([&](auto k) { read_one(k, cw, chs, 0, f0); });
+    // K step j (0..2) of the chunk: its MFMAs from cur, step j + 1 read into nxt
+    auto step = [&](auto nl_c, const Frags& cur, Frags& nxt, int j) __attribute__((always_inline)) {
+      constexpr int NM = Q * decltype(nl_c)::value + R * XP;
+      static_for<(NM > NR ? NM : NR)>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I < NM) mfma_one(nl_c, i, cur);
+        if constexpr (I < NR) read_one(i, cw, chs, j + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // One chunk.  Step 3 takes the barrier after its first PRE MFMAs: this
+    // wave's loads of chunk c + 1 have landed and its reads of chunk c are
+    // done (the last were issued during step 2), and after the barrier every
+    // wave's are; the chunk's stages then take H(c + 2) and W(c + 3), and the
+    // step's other MFMAs cover the reads of the next chunk's step 0.  (After
+    // the last chunk this loads the last chunk again and reads stages that
+    // are not used: every wave takes the same steps.)
     auto chunk = [&](auto nl_c) __attribute__((always_inline)) {
-      read_frags(cw, chs, 2, fr[2]);
-      mfma_step(nl_c, fr[0]);
-      read_frags(cw, chs, 3, fr[3]);
-      mfma_step(nl_c, fr[1]);
-      // this wave's loads of chunk c + 1 have landed and its reads of chunk
-      // c are done: after the barrier, every wave's
+      constexpr int NM = Q * decltype(nl_c)::value + R * XP;
+      constexpr int PRE = NM - NR > 2 ? NM - NR : (NM < 2 ? NM : 2);
+      step(nl_c, f0, f1, 0);
+      step(nl_c, f1, f0, 1);
+      step(nl_c, f0, f1, 2);
+      static_for<PRE>([&](auto i) {
+        mfma_one(nl_c, i, f1);
+        __builtin_amdgcn_sched_barrier(0);
+      });
       wait_vm_lgkm0<TW>();
       raw_barrier();
-      issue_h();
-      issue_w();
+      // the loads of H(c + 2), then W(c + 3), two after each MFMA
+      unsigned char* const hdst = hbase + lhc.stage * HBUF;
+      const int hso = kc_of(lhc.kci) * kRB;
+      unsigned char* const wdst = smem + lw.stage * WBUF;
+      const int wso = lw.pass * WROWS * row_bytes + kc_of(lw.kci) * kRB;
+      lhc.step(total, nch);
+      lw.step(total, nch);
+      auto load_one = [&](auto k_c) __attribute__((always_inline)) {
+        constexpr int k = decltype(k_c)::value;
+        if constexpr (k < TH)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, LOPA_LDS(hdst + (4 * k + w) * 1024), 16,
+                                                   hv[k], hso, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wr, LOPA_LDS(wdst + (4 * (k - TH) + w) * 1024), 16, wv,
+              wso + 32 * (k - TH) * row_bytes, 0, kWeightAux);
+      };
       cw = cw + 1 == kWideWStages ? 0 : cw + 1;
       chs = chs + 1 == kWideHStages ? 0 : chs + 1;
-      read_frags(cw, chs, 0, fr[0]);
-      mfma_step(nl_c, fr[2]);
-      read_frags(cw, chs, 1, fr[1]);
-      mfma_step(nl_c, fr[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int NLD = TH + TW, NSLOT = NM - PRE > NR ? NM - PRE : NR;
+      constexpr int LPS = (NLD + NSLOT - 1) / NSLOT;   // loads per slot
+      static_for<NSLOT>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I < NM - PRE) mfma_one(nl_c, std::integral_constant<int, PRE + I>{}, f1);
+        static_for<LPS>([&](auto q) {
+          constexpr int k = I * LPS + decltype(q)::value;
+          if constexpr (k < NLD) load_one(std::integral_constant<int, k>{});
+        });
+        if constexpr (I < NR) read_one(i, cw, chs, 0, f0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     auto run_pass = [&](auto nl_c, auto masked_c, int pass) __attribute__((always_inline)) {
       for (int kk = 0; kk < nch; ++kk) chunk(nl_c);
