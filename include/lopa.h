@@ -95,6 +95,27 @@ const char* lopa_status_string(int status);
 int lopa_workspace_bytes(const lopa_dims* dims, size_t* bytes);
 
 /*
+ * Initial pass of a block: the LM-head rows of the block as it stands, with
+ * no branch yet -- slot 0 alone, every masked position listed.  Its LM head
+ * gives the confidences and tokens the first explore step starts from (the
+ * news article above, section "LoPA 的核心设计：前瞻并行与分支验证": each step
+ * explores from the confidences the previous verification produced; for a
+ * new block that is one plain forward of the block).
+ *
+ * In  tok[B]  int32  block tokens, LOPA_MASK_TOKEN where masked
+ * Out nb[1]                 int32  1
+ *     rows[nb_max*B]        int32  the masked positions p, ascending, in
+ *                                  rows[0 .. m); 0 in the rest
+ *     row_ptr[nb_max+1]     int32  {0, m, m, ..., m}
+ *     conf[nb_max*B], arg[nb_max*B]  (optional, NULL to skip) the LM head's
+ *                                  outputs, cleared to 0 / -1 so unlisted
+ *                                  rows read as filled
+ * Bit-exact; one wavefront; no host synchronisation.
+ */
+int lopa_block_rows(const lopa_dims* dims, const int32_t* tok, int32_t* nb, int32_t* rows,
+                    int32_t* row_ptr, float* conf, int32_t* arg, hipStream_t stream);
+
+/*
  * Explore: build the anchor branch and up to k lookahead branches.
  *
  * In  tok[B]  int32  block tokens, LOPA_MASK_TOKEN where masked

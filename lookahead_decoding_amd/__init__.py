@@ -78,6 +78,7 @@ _SIGS = {
     "lopa_abi_version": ([], ctypes.c_int),
     "lopa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "lopa_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "lopa_block_rows": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "lopa_branch_build": ([ctypes.POINTER(Dims), _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
                           ctypes.c_int),
     "lopa_branch_build_floor": ([ctypes.POINTER(Dims), _I, ctypes.c_float, ctypes.c_float] +
@@ -174,6 +175,15 @@ def workspace_bytes(dims: Dims) -> int:
     n = ctypes.c_size_t(0)
     _check("lopa_workspace_bytes", lib().lopa_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
     return n.value
+
+
+def lopa_block_rows(dims, tok, nb, rows, row_ptr, conf=None, arg=None, stream=None) -> None:
+    import torch
+    i32, f32 = torch.int32, torch.float32
+    _check("lopa_block_rows", lib().lopa_block_rows(
+        ctypes.byref(dims), _ptr(tok, i32, "tok"), _ptr(nb, i32, "nb"), _ptr(rows, i32, "rows"),
+        _ptr(row_ptr, i32, "row_ptr"), _ptr(conf, f32, "conf"), _ptr(arg, i32, "arg"),
+        _stream(stream)))
 
 
 def lopa_branch_build(dims, k, tau, tok, conf, arg, nb, br_tok, br_mask, rows, row_ptr,

@@ -185,6 +185,48 @@ k_branch_select(int B, int nb_max, const int32_t* __restrict__ nb_ptr,
 
 }  // namespace lopa
 
+namespace lopa {
+
+// Initial pass of a block: slot 0 alone, every masked position listed.  Lane
+// p owns position p; the rows are a ballot compaction (ascending p).  The
+// other slots' rows and the LM head's outputs are cleared, so a position
+// that is not listed reads as filled (conf 0, arg -1).
+__global__ void __launch_bounds__(64)
+k_block_rows(int B, int nb_max, const int32_t* __restrict__ tok, int32_t* __restrict__ nb_out,
+             int32_t* __restrict__ rows, int32_t* __restrict__ row_ptr,
+             float* __restrict__ conf, int32_t* __restrict__ arg) {
+  __shared__ int pos[64];
+  const int p = threadIdx.x;
+  const bool masked = p < B && tok[p] == LOPA_MASK_TOKEN;
+  const unsigned long long bits = __ballot(masked);
+  const int m = __popcll(bits);
+  const int rank = __popcll(bits & ((1ull << p) - 1ull));
+  if (masked) pos[rank] = p;
+  __syncthreads();
+  const int n = nb_max * B;
+  for (int i = p; i < n; i += 64) rows[i] = i < m ? pos[i] : 0;
+  for (int i = p; i <= nb_max; i += 64) row_ptr[i] = i == 0 ? 0 : m;
+  if (p == 0) nb_out[0] = 1;
+  if (conf)
+    for (int i = p; i < n; i += 64) conf[i] = 0.f;
+  if (arg)
+    for (int i = p; i < n; i += 64) arg[i] = -1;
+}
+
+}  // namespace lopa
+
+extern "C" int lopa_block_rows(const lopa_dims* dims, const int32_t* tok, int32_t* nb,
+                               int32_t* rows, int32_t* row_ptr, float* conf, int32_t* arg,
+                               hipStream_t stream) {
+  int st = lopa_check_dims(dims);
+  if (st != LOPA_OK) return st;
+  if (!tok || !nb || !rows || !row_ptr) return LOPA_ERR_INVALID;
+  hipLaunchKernelGGL(lopa::k_block_rows, dim3(1), dim3(64), 0, stream, dims->B, dims->k_max + 1,
+                     tok, nb, rows, row_ptr, conf, arg);
+  LOPA_LAUNCH_CHECK();
+  return LOPA_OK;
+}
+
 extern "C" int lopa_branch_build(const lopa_dims* dims, int32_t k, float tau,
                                  const int32_t* tok, const float* conf, const int32_t* arg,
                                  int32_t* nb, int32_t* br_tok, uint8_t* br_mask,

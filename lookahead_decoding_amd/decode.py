@@ -20,10 +20,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (MASK, lopa_branch_attn, lopa_branch_build, lopa_branch_build_floor,
-               lopa_branch_select,
-               lopa_branch_select_alpha, lopa_lmhead_conf, lopa_lmhead_conf_ent,
-               lopa_lmhead_sample, lopa_synth_qkv)
+from . import (MASK, lopa_block_rows, lopa_branch_attn, lopa_branch_build,
+               lopa_branch_build_floor, lopa_branch_select, lopa_branch_select_alpha,
+               lopa_lmhead_conf, lopa_lmhead_conf_ent, lopa_lmhead_sample, lopa_synth_qkv)
 from .step import StepBuffers
 
 
@@ -62,15 +61,10 @@ def start_block(dims, seed, tok0, Kp, Vp, W, buf: DecodeBuffers, stream=None,
     dev = buf.tok.device
     B = dims.B
     buf.tok.copy_(torch.from_numpy(tok0).to(dev))
-    masked = np.flatnonzero(tok0 == MASK).astype(np.int32)
-    buf.rows0.zero_()
-    buf.rows0[:len(masked)] = torch.from_numpy(masked).to(dev)
-    buf.row_ptr0.fill_(len(masked))
-    buf.row_ptr0[0] = 0
+    # rows of the masked positions, the LM head's outputs cleared (on the device)
+    lopa_block_rows(dims, buf.tok, buf.one, buf.rows0, buf.row_ptr0, buf.conf, buf.arg, stream)
     lopa_synth_qkv(dims, seed, buf.tok, buf.one, buf.Qb, buf.Kb, buf.Vb, stream)
     lopa_branch_attn(dims, Kp, Vp, buf.Qb, buf.Kb, buf.Vb, buf.one, buf.H, buf.ws, stream)
-    buf.conf.zero_()
-    buf.arg.fill_(-1)
     if temperature is None:
         lopa_lmhead_conf(dims, buf.H, W, buf.rows0, buf.row_ptr0, buf.one, buf.conf, buf.arg,
                          None, buf.ws, stream)

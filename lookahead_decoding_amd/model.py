@@ -9,8 +9,9 @@ once a block is decoded.
 """
 from __future__ import annotations
 
-from . import (ModelDims, lopa_branch_build, lopa_branch_forward, lopa_branch_select,
-               lopa_lmhead_conf, lopa_model_synth, model_layout, model_workspace_bytes)
+from . import (ModelDims, lopa_block_rows, lopa_branch_build, lopa_branch_forward,
+               lopa_branch_select, lopa_lmhead_conf, lopa_model_synth, model_layout,
+               model_workspace_bytes)
 
 # A block decoded with the model repeats the step above from the initial
 # pass's state until no position is masked (model_decode_block), and
@@ -128,21 +129,15 @@ def model_decode_block(model: Model, dims, k: int, tau: float, tok0, buf: ModelD
     s + 1 after step s."""
     import numpy as np
     import torch
-    from . import MASK
     tok0 = np.asarray(tok0, np.int32)
     dev = buf.tok.device
     B, nbm = dims.B, dims.nb_max
     s = buf.step
     buf.tok.copy_(torch.from_numpy(tok0).to(dev))
-    buf.tok0.copy_(torch.from_numpy(np.tile(tok0, nbm)).to(dev))
-    masked = np.flatnonzero(tok0 == MASK).astype(np.int32)
-    buf.rows0.zero_()
-    buf.rows0[:len(masked)] = torch.from_numpy(masked).to(dev)
-    buf.row_ptr0.fill_(len(masked))
-    buf.row_ptr0[0] = 0
+    buf.tok0.view(nbm, B).copy_(buf.tok.expand(nbm, B))
+    # rows of the masked positions, the LM head's outputs cleared (on the device)
+    lopa_block_rows(dims, buf.tok, buf.one, buf.rows0, buf.row_ptr0, s.conf, s.arg, stream)
     forward(model, buf.tok0, buf.one, buf.fwd, stream, dims=dims)
-    s.conf.zero_()
-    s.arg.fill_(-1)
     lopa_lmhead_conf(dims, buf.fwd.H, model.lm_head, buf.rows0, buf.row_ptr0, buf.one, s.conf,
                      s.arg, None, s.ws, stream)
     buf.conf.copy_(s.conf[:B])

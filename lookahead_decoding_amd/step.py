@@ -7,8 +7,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (BF16, F32, MASK, Dims, lopa_branch_attn, lopa_branch_build,
-               lopa_branch_select, lopa_lmhead_conf, workspace_bytes)
+from . import (BF16, F32, Dims, lopa_block_rows, lopa_branch_attn,
+               lopa_branch_build, lopa_branch_select, lopa_lmhead_conf, workspace_bytes)
 
 
 def dims_of(cfg) -> Dims:
@@ -72,14 +72,13 @@ def initial_pass(dims: Dims, tok: np.ndarray, x: dict, buf: StepBuffers, stream=
     import torch
     dev = buf.H.device
     B = dims.B
-    masked = np.flatnonzero(np.asarray(tok) == MASK).astype(np.int32)
-    nb1 = torch.ones(1, dtype=torch.int32, device=dev)
-    rows = torch.zeros(dims.nb_max * B, dtype=torch.int32, device=dev)
-    rows[:len(masked)] = torch.from_numpy(masked).to(dev)
-    row_ptr = torch.full((dims.nb_max + 1,), len(masked), dtype=torch.int32, device=dev)
-    row_ptr[0] = 0
+    tok_d = to_device(np.asarray(tok, np.int32), dev)
+    nb1 = torch.empty(1, dtype=torch.int32, device=dev)
+    rows = torch.empty(dims.nb_max * B, dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(dims.nb_max + 1, dtype=torch.int32, device=dev)
+    conf = torch.empty(dims.nb_max * B, dtype=torch.float32, device=dev)
+    arg = torch.empty(dims.nb_max * B, dtype=torch.int32, device=dev)
+    lopa_block_rows(dims, tok_d, nb1, rows, row_ptr, conf, arg, stream)
     lopa_branch_attn(dims, x["Kp"], x["Vp"], x["Qb"], x["Kb"], x["Vb"], nb1, buf.H, buf.ws, stream)
-    conf = torch.zeros(dims.nb_max * B, dtype=torch.float32, device=dev)
-    arg = torch.full((dims.nb_max * B,), -1, dtype=torch.int32, device=dev)
     lopa_lmhead_conf(dims, buf.H, x["W"], rows, row_ptr, nb1, conf, arg, None, buf.ws, stream)
     return conf[:B].clone(), arg[:B].clone()

@@ -77,6 +77,12 @@ def test_null_pointers_and_k_rejected():
     assert L.lopa_branch_select(ctypes.byref(d), *([fake] * 9), None, None) == -1
     assert L.lopa_lmhead_conf(None, *([fake] * 8), fake, 1 << 30, None) == -1
     assert L.lopa_synth_qkv(ctypes.byref(d), 1, None, fake, fake, fake, fake, None) == -1
+    # initial-pass rows: tok, nb, rows and row_ptr are required (conf / arg optional)
+    for i in range(4):
+        args = [fake] * 4
+        args[i] = None
+        assert L.lopa_block_rows(ctypes.byref(d), *args, None, None, None) == -1
+    assert L.lopa_block_rows(None, *([fake] * 6), None) == -1
     # confidence-floor explore: NaN floor, k out of range, null arrays
     assert L.lopa_branch_build_floor(ctypes.byref(d), 0, 0.9, float("nan"), *([fake] * 8),
                                      None) == -1

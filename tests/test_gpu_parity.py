@@ -83,6 +83,48 @@ def test_gpu_build_edges(case):
     assert_build_equal(g, O.branch_build(tok, conf, arg, k, np.float32(0.9), k_max + 1))
 
 
+@pytest.mark.parametrize("B,k_max,case", [(1, 0, "rand"), (17, 4, "rand"), (32, 4, "rand"),
+                                            (64, 15, "rand"), (64, 15, "none"), (64, 15, "all"),
+                                            (33, 1, "last"), (64, 8, "first")])
+def test_gpu_block_rows(B, k_max, case):
+    """Initial-pass rows on the device: every masked position, ascending, in
+    slot 0; the other slots empty; the LM head's outputs cleared."""
+    rng = np.random.default_rng(B * 100 + k_max)
+    tok = rng.integers(0, 5000, B).astype(np.int32)
+    if case == "rand":
+        tok[rng.random(B) < 0.5] = M
+    elif case == "all":
+        tok[:] = M
+    elif case == "last":
+        tok[-1] = M
+    elif case == "first":
+        tok[0] = M
+    dims = lopa.Dims(L=0, B=B, Hq=1, Hkv=1, d=8, V=5000, k_max=k_max, dtype=lopa.F32)
+    n = (k_max + 1) * B
+    dev = "cuda"
+    nb = torch.full((1,), 7, dtype=torch.int32, device=dev)
+    rows = torch.full((n,), 12345, dtype=torch.int32, device=dev)
+    row_ptr = torch.full((k_max + 2,), -9, dtype=torch.int32, device=dev)
+    conf = torch.full((n,), 3.5, dtype=torch.float32, device=dev)
+    arg = torch.full((n,), 77, dtype=torch.int32, device=dev)
+    lopa.lopa_block_rows(dims, to_device(tok), nb, rows, row_ptr, conf, arg)
+    torch.cuda.synchronize()
+    masked = np.flatnonzero(tok == M)
+    want_rows = np.zeros(n, np.int32)
+    want_rows[:len(masked)] = masked
+    want_ptr = np.full(k_max + 2, len(masked), np.int32)
+    want_ptr[0] = 0
+    assert int(nb.item()) == 1
+    assert np.array_equal(rows.cpu().numpy(), want_rows)
+    assert np.array_equal(row_ptr.cpu().numpy(), want_ptr)
+    assert np.all(conf.cpu().numpy() == 0.0) and np.all(arg.cpu().numpy() == -1)
+    # conf / arg may be left out
+    rows.fill_(5)
+    lopa.lopa_block_rows(dims, to_device(tok), nb, rows, row_ptr)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), want_rows)
+
+
 # ---------------------------------------------------------------------------
 # select
 # ---------------------------------------------------------------------------
