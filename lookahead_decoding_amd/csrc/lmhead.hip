@@ -26,8 +26,11 @@
 //                   device and picks the body and the row groups; the
 //                   groups of one vocabulary range share the weight stream
 //                   through L2.
-//   k_lmhead_plain  float32 (and shapes outside the MFMA kernel): one thread
-//                   per vocabulary entry, FMA dot products.
+//   k_lmhead_f32    float32: v_mfma_f32_32x32x2_f32 tiles of 256 vocabulary
+//                   entries x 32 rows, staged through LDS.
+//   k_lmhead_plain  bf16 shapes outside the MFMA kernels (hidden not a
+//                   multiple of 64): one thread per vocabulary entry, FMA
+//                   dot products.
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -1120,6 +1123,104 @@ k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int h_bytes,
 }
 
 // ---------------------------------------------------------------------------
+// float32 MFMA kernel
+// ---------------------------------------------------------------------------
+//
+// A workgroup takes one tile of 256 vocabulary entries against one tile of
+// 32 listed rows; wave w multiplies entries 64w .. 64w + 63 (two 32 x 32
+// output tiles) with v_mfma_f32_32x32x2_f32 (A: weight rows, B: activation
+// rows, so a lane holds 16 logits of one row, laid out as in the bf16
+// kernels).  K runs in chunks of 32: the workgroup stages the chunk of its
+// weight and activation rows in LDS with coalesced loads (zeros past V, the
+// listed rows and hidden; rows padded to 33 floats against bank conflicts),
+// then every wave reads its fragments from there.  The fold and the partials
+// are the bf16 kernels': one partial per (row, 256-entry tile), merged by
+// k_lmhead_merge.
+constexpr int kF32KC = 32;
+constexpr int kF32Stride = kF32KC + 1;
+
+template <int MODE>
+__global__ void __launch_bounds__(256)
+k_lmhead_f32(int V, int hidden, int ntiles, int nb_max, int m_max, const float* __restrict__ H,
+             const float* __restrict__ W, const int32_t* __restrict__ rows,
+             const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ nb_ptr,
+             float* __restrict__ ws_m, float* __restrict__ ws_s, int32_t* __restrict__ ws_i,
+             float* __restrict__ ws_t, float* __restrict__ ws_z, const Sampling smp,
+             float* __restrict__ logits_out) {
+  using RP = typename std::conditional<MODE == kModeSample, SPartial, Partial>::type;
+  __shared__ float wl[kPlainVocabPerWG * kF32Stride];
+  __shared__ float hl[32 * kF32Stride];
+  __shared__ RP red[4][32];
+  const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
+  const int t0 = blockIdx.y * 32;
+  if (t0 >= M) return;
+  const int v0 = blockIdx.x * kPlainVocabPerWG;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  for (int k0 = 0; k0 < hidden; k0 += kF32KC) {
+    __syncthreads();   // the previous chunk's reads are done
+    for (int e = tid; e < kPlainVocabPerWG * kF32KC; e += 256) {
+      const int r = e / kF32KC, kk = e % kF32KC;
+      const int v = v0 + r, k = k0 + kk;
+      wl[r * kF32Stride + kk] = v < V && k < hidden ? W[static_cast<size_t>(v) * hidden + k] : 0.f;
+    }
+    for (int e = tid; e < 32 * kF32KC; e += 256) {
+      const int r = e / kF32KC, kk = e % kF32KC;
+      const int m = t0 + r, k = k0 + kk;
+      hl[r * kF32Stride + kk] =
+          m < M && k < hidden ? H[static_cast<size_t>(rows[m]) * hidden + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kF32KC; kk += 2) {
+      const float b = hl[ln * kF32Stride + kk + lh];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const float a = wl[(w * 64 + n * 32 + ln) * kF32Stride + kk + lh];
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // acc[n][q]: logit of listed row t0 + ln, vocabulary entry
+  // v0 + 64w + 32n + 4lh + kTileOff(q)
+  const int m = t0 + ln;
+  RP p;
+  if constexpr (MODE == kModeSample) p = empty_spartial();
+  else p = empty_partial();
+  const unsigned pos =
+      MODE == kModeSample ? static_cast<unsigned>(rows[min(m, M - 1)] % smp.B) : 0u;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int vb = v0 + w * 64 + n * 32;
+    fold_tile_mode<MODE, true>(p, acc[n], vb, lh, V, smp, pos);
+    if (logits_out && m < M) {
+      const size_t lb = static_cast<size_t>(rows[m]) * V;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int v = vb + 4 * lh + kTileOff(q);
+        if (v < V) logits_out[lb + v] = acc[n][q];
+      }
+    }
+  }
+  p = merge(p, shfl_xor(p, 32));
+  if (lh == 0) red[w][ln] = p;
+  __syncthreads();
+  if (tid < 32 && t0 + tid < M) {
+    RP q = merge(merge(red[0][tid], red[1][tid]), merge(red[2][tid], red[3][tid]));
+    const size_t o = static_cast<size_t>(t0 + tid) * ntiles + blockIdx.x;
+    ws_m[o] = q.m;
+    ws_s[o] = q.s;
+    ws_i[o] = q.i;
+    if constexpr (MODE == kModeEnt) ws_t[o] = q.t;
+    if constexpr (MODE == kModeSample) {
+      ws_t[o] = q.g;
+      ws_z[o] = q.z;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Plain path
 // ---------------------------------------------------------------------------
 
@@ -1290,10 +1391,10 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
   } else {
     const dim3 grid(p.ntiles, p.m_max);
     if (dims->dtype == LOPA_F32) {
-      hipLaunchKernelGGL((k_lmhead_plain<float, MODE>), grid, dim3(256), 0, stream, V, hidden,
-                         p.ntiles, nb_max, p.m_max, static_cast<const float*>(H),
-                         static_cast<const float*>(W), rows, row_ptr, nb, wm, wsum, wi, wt, wz,
-                         smp, logits_out);
+      hipLaunchKernelGGL(k_lmhead_f32<MODE>, dim3(p.ntiles, (p.m_max + 31) / 32), dim3(256), 0,
+                         stream, V, hidden, p.ntiles, nb_max, p.m_max,
+                         static_cast<const float*>(H), static_cast<const float*>(W), rows,
+                         row_ptr, nb, wm, wsum, wi, wt, wz, smp, logits_out);
     } else {
       hipLaunchKernelGGL((k_lmhead_plain<unsigned short, MODE>), grid, dim3(256), 0, stream, V,
                          hidden, p.ntiles, nb_max, p.m_max, Hb, Wb, rows, row_ptr, nb, wm, wsum,

@@ -284,6 +284,11 @@ def test_gpu_attn_scores_outgrow_the_first_units(L):
 
 HEAD_CASES = [
     ("f32-tiny", dict(), None),
+    # the float32 MFMA kernel: a hidden size that is not a multiple of its
+    # 32-wide K chunk, a vocabulary that is not a multiple of its 256-entry
+    # tile (and one smaller than a tile), three 32-row tiles, the last ragged
+    ("f32-hidden30-V1001-90rows", dict(Hq=3, Hkv=3, d=10, V=1001, B=32, m=30, k=2), None),
+    ("f32-V100-1row", dict(Hq=2, Hkv=1, d=40, V=100, B=4, m=1, k=0), None),
     ("bf16-mfma-ragged-V", dict(dtype="bf16", Hq=4, Hkv=2, d=64, V=1000, B=16, m=12, k=3), None),
     ("bf16-mfma-two-groups", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=700, B=64, m=64, k=15), None),
     ("bf16-plain-hidden96", dict(dtype="bf16", Hq=3, Hkv=1, d=32, V=513, B=8, m=6, k=2), None),
