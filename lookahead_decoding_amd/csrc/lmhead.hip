@@ -879,8 +879,12 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     // slot of LDS (volatile, so the round trip stays): the matrix registers
     // that hold the accumulators are stored as they are, and the fold reads
     // ordinary registers back, one tile at a time.
-    volatile f32x4* fslot =
-        reinterpret_cast<volatile f32x4*>(smem + kWideSmem + w * kWideFoldSlot) + lane;
+    // (an LDS-typed pointer: through a generic one the round trip became
+    // flat accesses, each waited on in full)
+    using lds_f32x4 = __attribute__((address_space(3))) f32x4;
+    volatile lds_f32x4* fslot =
+        reinterpret_cast<volatile lds_f32x4*>(static_cast<unsigned>(
+            reinterpret_cast<uintptr_t>(smem + kWideSmem + w * kWideFoldSlot))) + lane;
     auto through_lds = [&](const f32x16& a) __attribute__((always_inline)) {
       f32x16 r;
 #pragma unroll
