@@ -40,10 +40,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 HEAD_SOURCES = ("lmhead.hip", "head_plan.hpp", "stream_tile.hpp", "lopa_common.hpp")
 ATTN_SOURCES = ("attn.hip", "attn_plan.hpp", "lopa_common.hpp")
 HEAD_TRAFFIC = {
-    "7b-bf16-L512-B32-m24-k4": ("f04888885469cff3", 1104599970),
-    "7b-bf16-L2048-B32-m28-k8": ("f04888885469cff3", 1111049671),
-    "7b-bf16-L1024-B32-m24-k15": ("f04888885469cff3", 1115787976),
-    "7b-bf16-L4096-B64-m48-k8": ("f04888885469cff3", 1158123918),
+    "7b-bf16-L512-B32-m24-k4": ("076bdf0f96aa0ae2", 1104577980),
+    "7b-bf16-L2048-B32-m28-k8": ("076bdf0f96aa0ae2", 1111015075),
+    "7b-bf16-L1024-B32-m24-k15": ("076bdf0f96aa0ae2", 1115874322),
+    "7b-bf16-L4096-B64-m48-k8": ("076bdf0f96aa0ae2", 1158616338),
 }
 ATTN_TRAFFIC = {
     "7b-bf16-L512-B32-m24-k4": ("b83e9d0f5e96b081", 26936320),
