@@ -207,12 +207,16 @@ int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc): the same kernels and results as
  * lopa_lmhead_conf, bit for bit, with its partials in a fixed array inside
- * the library (5 MiB per device, held by every device the library runs on
+ * the library (16 MiB per device, held by every device the library runs on
  * until the process ends).  The call itself allocates nothing; on its first
  * call on a device it looks up that device's copy of the array.
- *   Returns LOPA_ERR_TOO_LARGE (nothing launched) when the partials would not
- *   fit: never for bfloat16 shapes the MFMA kernels take; for the float32
- *   path when nb_max*B x ceil(V / 256) > 262144.
+ *   Returns LOPA_ERR_TOO_LARGE (nothing launched) when what lopa_lmhead_conf
+ *   would take from its workspace does not fit: for bfloat16 shapes the MFMA
+ *   kernels take, only when the wide kernel's operand-ordered copy of the
+ *   rows (nb_max*B rounded up to 32, x Hq*d x 2 bytes, taken when
+ *   nb_max*B >= 161 and Hq*d % 128 == 0) passes 11 MiB (1024 rows at
+ *   Hq*d = 5632 still fit); for the float32 path when
+ *   nb_max*B x ceil(V / 256) > 838860.
  *   Every call on a device uses that device's one array and leaves it
  *   holding its partials: calls that overlap on one device (different
  *   streams, or host threads without ordering) race.  Calls ordered on one

@@ -71,19 +71,22 @@ __host__ __device__ inline HeadGroups head_groups(int M) {
 
 // The wide kernel (k_lmhead_wide): four waves, one per SIMD, each of them
 // both loading and computing, with large register tiles.  Its row groups
-// hold at most kWideMaxTiles 32-row tiles (the LDS ring holds every row of a
-// group); th = 4q + r tiles per group: each wave owns q tiles against every
-// weight tile of a pass, and the r remaining tiles are shared out by weight
-// tile (wave w takes weight tiles w, w + 4, ...), so every wave runs the
-// same number of MFMAs.  tw: weight tiles per pass (8 while the LDS allows
-// it, else 4).  It serves the row-tile counts where it measured faster than
-// the narrow kernel (k_lmhead_mfma) in a same-box comparison at every count
-// from 5 to 32 tiles at the 7B shapes: 6, 9, 13, 17 and 18 tiles (by 3, 8,
-// 2, 4 and 2 %); the narrow kernel serves every other count.  At 5 tiles it
-// measured 12 % faster as well, but the row count lives on the device, so a
-// call that may reach the wide kernel launches both and the idle one costs
-// about 5 us: a call of at most 5 tiles (block 32, 5 branches: m_max = 160)
-// launches the narrow kernel alone.
+// hold at most kWideMaxTiles 32-row tiles; th = 4q + r tiles per group: each
+// wave owns q tiles against every weight tile of a pass, and the r remaining
+// tiles are shared out by weight tile (wave w takes weight tiles w, w + 4,
+// ...), so every wave runs the same number of MFMAs.  tw: weight tiles per
+// pass (8 up to 7 row tiles, else 4).  The weight streams through an LDS
+// ring; the activation fragments go straight from an operand-ordered copy
+// (made per call) into registers.  It serves the row-tile counts where it
+// measured faster than the narrow kernel (k_lmhead_mfma) in a same-box
+// comparison at the 7B shapes (6 and 9..32 tiles): 6, 9-14, 17-20 and 23-26
+// tiles (by 3-20 %; 19, 23 and 25 by their layouts' neighbours); the narrow
+// kernel serves every other count (at 7, 8, 15, 16, 22 and 27-32 tiles it
+// measured equal or up to 12 % faster).  At 5 tiles the wide kernel measured
+// 17 % faster as well, but the row count lives on the device, so a call that
+// may reach the wide kernel launches both and the idle one costs about 5 us:
+// a call of at most 5 tiles (block 32, 5 branches: m_max = 160) launches the
+// narrow kernel alone.
 constexpr int kWideMinTiles = 6;
 constexpr int kWideMaxTiles = 13;
 
@@ -100,7 +103,14 @@ __host__ __device__ inline WideGroups wide_groups(int M) {
 
 __host__ __device__ inline bool wide_takes(int M) {
   const int t = (M + 31) / 32;
-  return t == 6 || t == 9 || t == 13 || t == 17 || t == 18;
+  return t == 6 || (t >= 9 && t <= 14) || (t >= 17 && t <= 20) || t == 23 || t == 24 ||
+         t == 25 || t == 26;
+}
+
+// Whether a call with m_max rows may reach the wide kernel (its K loop takes
+// 128 hidden values per round).
+inline bool wide_possible(int m_max, int hidden) {
+  return (m_max + 31) / 32 >= kWideMinTiles && hidden % 128 == 0;
 }
 
 // Vocabulary parts per row of whichever MFMA kernel serves M rows (wide:
@@ -127,9 +137,14 @@ inline long long head_part_bytes_max(const lopa_dims& d) {
 // Per (row, vocabulary tile) partial: max logit (float), scaled sum (float),
 // argmax or sample (int32), entropy term or perturbed best score (float),
 // scaled logit of the sample (float) -- five planes of m_max * ntiles.
+// When the wide kernel may run, an operand-ordered copy of the activation
+// rows follows (256-byte aligned): m_max rounded up to 32 rows x hidden bf16.
 inline size_t lmhead_workspace_bytes(const lopa_dims& d) {
   const HeadPlan p = head_plan(d);
-  return static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 20u;
+  const size_t partials = static_cast<size_t>(p.m_max) * static_cast<size_t>(p.ntiles) * 20u;
+  if (!p.mfma || !wide_possible(p.m_max, d.Hq * d.d)) return partials;
+  return (partials + 255) / 256 * 256 +
+         static_cast<size_t>((p.m_max + 31) / 32) * 32 * static_cast<size_t>(d.Hq * d.d) * 2;
 }
 
 }  // namespace lopa

@@ -26,6 +26,12 @@
 //                   device and picks the body and the row groups; the
 //                   groups of one vocabulary range share the weight stream
 //                   through L2.
+//   k_lmhead_wide   bf16, 6 or more row tiles (the counts wide_takes()
+//                   names): four waves that load and compute, register
+//                   tiles of up to 13 row tiles, the weight through an LDS
+//                   ring, the activation fragments straight into registers
+//                   from an operand-ordered copy that k_lmhead_hfrag makes
+//                   first.
 //   k_lmhead_f32    float32: v_mfma_f32_32x32x2_f32 tiles of 256 vocabulary
 //                   entries x 32 rows, staged through LDS.
 //   k_lmhead_plain  bf16 shapes outside the MFMA kernels (hidden not a
@@ -48,6 +54,8 @@ namespace lopa {
 
 
 // Calls f(integral_constant<int, i>) for i = 0 .. N-1.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -536,33 +544,39 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
 //
 // Four waves (one per SIMD, up to 512 registers each) hold large register
 // tiles: wave w owns q activation tiles against all tw weight tiles of a
-// pass (q tw MFMAs per 16-wide K step from tw + q fragments), plus its share
-// of the r remaining activation tiles (their pairs with weight tiles w,
-// w + 4, ...): at 13 tiles every wave runs 13 MFMAs per step from 9
-// fragments, where the narrow kernel's 2 x 2 tiles read 4 fragments for 4.
-// The accumulators live in the matrix (AGPR) registers.  Every wave also
-// issues its share of the loads that fill the LDS rings (the weight: three
-// stages, two chunks in flight; the group's activation rows: two stages, one
-// chunk in flight, from L2), so no wave is spent on loading alone.  One
-// barrier per K chunk, taken in the chunk's last K step after its first few
-// MFMAs: by then this wave's reads of the chunk are done (they run one step
-// ahead), and the step's remaining MFMAs carry the loads into the freed
-// stages and the reads of the next chunk's first step.  With one wave per
-// SIMD nothing else hides a wait on LDS, so each MFMA is followed by one
-// read of the next step and the order is pinned with scheduling barriers;
-// the compiler's own order put reads next to their MFMAs and waited on them
-// (13 tiles: 460-475 against 490-500 us per call, same box).  The barrier
-// waits for this wave's own loads of the next chunk (vmcnt) and its LDS
-// reads (lgkmcnt), and neither it nor the compiler lets memory accesses
-// move across it (a __syncthreads() would wait for every load in flight).
+// pass (q tw MFMAs per 16-wide K step), plus its share of the r remaining
+// activation tiles (their pairs with weight tiles w, w + 4, ...): at 13 tiles
+// every wave runs 13 MFMAs per step.  The accumulators live in the matrix
+// (AGPR) registers.  The weight streams through an LDS ring (4 to 7 stages,
+// as many as the LDS and the vector-memory counter allow), every wave
+// issuing its share of the buffer loads that write LDS; each weight fragment
+// read from LDS feeds q MFMAs.  The activation rows do not pass through LDS:
+// k_lmhead_hfrag first lays the listed rows out in MFMA operand order (one
+// 1 KB block per 32-row tile and 16-wide K step), and each wave loads its own
+// fragments from there straight into registers, one contiguous 1 KB read per
+// fragment, a chunk ahead (two register sets).  Staging them through LDS as
+// well (the layout before this one: two activation stages, each wave reading
+// 9 fragments per 13 MFMAs) took 460-475 us per call at 13 tiles against
+// 420-430 us here (same box).
 //
-// Measured against the narrow kernel (same box, 7B shapes): faster where
-// the narrow kernel changes layout (5, 6, 9, 17, 18 tiles) and by 2 % at 13,
-// slower elsewhere (before the pinned order above).  Timing-only copies at 13
-// tiles: the MFMAs with their fragment reads alone take about 380 us, the
-// loads with the reads alone about 365 us; each CU restages all 416
-// activation rows from L2 for every 128 weight rows, so the L2-to-LDS
-// traffic (about 5 GB a call) is what the MFMAs have to hide.
+// One barrier per K chunk, taken in the chunk's last K step after its first
+// few MFMAs: by then this wave's weight reads of the chunk are done (they run
+// one step ahead), and the step's remaining MFMAs carry the loads into the
+// freed stage and the reads of the next chunk's first step.  With one wave
+// per SIMD nothing else hides a wait, so each MFMA is followed by at most one
+// fragment read and one load and the order is pinned with scheduling
+// barriers (the compiler's own order put reads next to their MFMAs and
+// waited on them).  The barrier waits for this wave's own loads of the next
+// chunk (vmcnt) and its LDS reads (lgkmcnt), and neither it nor the compiler
+// lets memory accesses move across it (a __syncthreads() would wait for
+// every load in flight).
+//
+// What still bounds it (timing-only copies at 13 tiles, same box): the MFMAs
+// with their reads, barriers and folds alone take about 268 us; with the
+// weight stream but no activation loads 318 us; with both 420 us.  The
+// vector-memory counter completes in issue order, so waiting for an
+// activation fragment also waits for every older weight load: the weight's
+// HBM latency is covered only by the activation loads' one-chunk lead.
 
 // Entry r of a lane's 16 (the 32x32 MFMA output layout) lies at vocabulary
 // vb + 4h + kTileOff(r).  The folds below compare these compile-time offsets
@@ -668,10 +682,19 @@ __device__ __forceinline__ void fold_tile_mode(RP& p, const f32x16& a, int vb, i
 }
 
 constexpr int kWideThreads = 256;
-constexpr int kWideWStages = 3;
-constexpr int kWideHStages = 2;
-constexpr int kWideSmem = 152 * 1024;
-constexpr int kWideFoldSlot = 2048;   // bytes of LDS per wave for the fold's round trip
+constexpr int kWideSmem = 128 * 1024;      // the weight ring
+constexpr int kWideFoldSlot = 2048;        // bytes of LDS per wave for the fold's round trip
+
+// Stages of the weight ring: as many as the LDS and the vector-memory
+// counter allow (4..8).  A wave may have (S - 3) TW weight loads and
+// (S - 2) NH activation loads in flight when it waits for a weight chunk
+// (the loop's issue order), and the counter holds at most 63.
+template <int TW, int NH>
+constexpr int wide_stages() {
+  int s = 8;
+  while (s > 4 && ((s - 3) * TW + (s - 2) * NH > 63 || s * TW * 32 * kRB > kWideSmem)) --s;
+  return s;
+}
 
 // s_waitcnt vmcnt(VM) lgkmcnt(0)
 template <int VM>
@@ -704,30 +727,41 @@ struct LoadCursor {
   }
 };
 
-// Fragment reads of one K step of the wide body (TW weight tiles, Q own and
-// R remaining activation tiles, TW / 4 weight tiles paired with each
-// remaining one), in the order the step's MFMAs -- own tiles t-major, then
-// the remaining pairs -- first use them: w0, h0, w1 .. w(TW-1),
-// h1 .. h(Q-1), then xw0, h(Q) .. h(Q+R-1), xw1 ...  kind 0: weight tile,
-// 1: activation tile, 2: paired weight tile.
-template <int TW, int Q, int R>
-struct WideOrder {
-  static constexpr int XP = TW / 4;
-  static constexpr int count = TW + Q + (R > 0 ? R + XP : 0);
-  static constexpr int kind(int i) {
-    return i == 0 ? 0 : i == 1 ? 1 : i <= TW ? 0 : i < TW + Q ? 1 : i == TW + Q ? 2
-         : i <= TW + Q + R ? 1 : 2;
-  }
-  static constexpr int index(int i) {
-    return i == 0 ? 0 : i == 1 ? 0 : i <= TW ? i - 1 : i < TW + Q ? i - TW : i == TW + Q ? 0
-         : i <= TW + Q + R ? Q + (i - TW - Q - 1) : i - TW - Q - R;
-  }
-};
+// The activation rows in MFMA operand order, made once per call for the wide
+// kernel: fragment f = tile * (hidden / 16) + s holds, for lane l, the eight
+// values 16 s + 8 (l / 32) .. +8 of listed row 32 tile + l % 32 (rows past
+// the listed count repeat the last one), 16 bytes per lane, 1 KB per
+// fragment.  A wave then loads its activation fragments straight into
+// registers, each one 1 KB contiguous read from L2.
+__global__ void __launch_bounds__(256)
+k_lmhead_hfrag(int hidden, int nb_max, int m_max, int h_bytes,
+               const unsigned short* __restrict__ H, const int32_t* __restrict__ rows,
+               const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ nb_ptr,
+               u32x4* __restrict__ Hf) {
+  const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
+  if (!wide_takes(M)) return;
+  const int nks = hidden >> 4;
+  const int f = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tile = f / nks;
+  if (tile * 32 >= M) return;
+  const int lane = threadIdx.x & 63;
+  const int s = f - tile * nks;
+  const int r = rows[min(tile * 32 + (lane & 31), M - 1)];
+  const __amdgpu_buffer_rsrc_t hr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
+  Hf[static_cast<size_t>(f) * 64 + lane] =
+      __builtin_amdgcn_raw_buffer_load_b128(hr, r * hidden * 2 + s * 32 + (lane >> 5) * 16, 0, 0);
+}
+
+// Bytes of the operand-ordered activation copy for m_max rows.
+__host__ __device__ inline size_t hfrag_bytes(int m_max, int hidden) {
+  return static_cast<size_t>((m_max + 31) / 32) * 32 * hidden * 2;
+}
 
 template <int TW, int Q, int R, int MODE>
 __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int part, int Mg,
-                                          int row0, int h_bytes,
-                                          const unsigned short* __restrict__ H,
+                                          int row0, int hf_bytes,
+                                          const unsigned short* __restrict__ Hf,
                                           const unsigned short* __restrict__ W,
                                           const int32_t* __restrict__ rows, unsigned char* smem,
                                           float* __restrict__ ws_m, float* __restrict__ ws_s,
@@ -737,11 +771,20 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
   constexpr int TH = 4 * Q + R;          // activation tiles of the group
   constexpr int QR = Q + R;              // activation tiles this wave multiplies
   constexpr int WROWS = TW * 32;         // weight rows per pass
-  constexpr int WBUF = WROWS * kRB, HBUF = TH * 32 * kRB;
-  constexpr int XP = TW / 4;             // weight tiles per remaining activation tile per wave
+  constexpr int WBUF = WROWS * kRB;
+  constexpr int XP = R > 0 ? TW / 4 : 0; // weight tiles per remaining activation tile per wave
+  constexpr int XA = XP > 0 ? XP : 1;
   constexpr int KS = kKC / 16;           // MFMA K steps per chunk
+  constexpr int NH = QR * KS;            // activation fragment loads per chunk
+  constexpr int NR = TW + XP;            // weight fragment reads per K step
+  constexpr int S = wide_stages<TW, NH>();
+  // loads a wave may have in flight at a chunk's barrier: after the weight
+  // chunk it waits for come the activation loads of S - 2 chunks and S - 3
+  // weight chunks (the issue order of the loop below)
+  constexpr int VM_BAR = (S - 3) * TW + (S - 2) * NH;
   static_assert(TW % 4 == 0 && Q >= 1 && R >= 0 && R < 4 && TH <= kWideMaxTiles, "wide layout");
-  static_assert(kWideWStages * WBUF + kWideHStages * HBUF <= kWideSmem, "wide LDS");
+  static_assert(S >= 4 && S * WBUF <= kWideSmem, "wide LDS");
+  static_assert(VM_BAR < 64 && 2 * TW + NH < 64, "vmcnt range");
   static_assert(R * 4 * 32 * static_cast<int>(sizeof(RP)) <= kWideSmem, "merge area");
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -751,10 +794,9 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
   const int v_lo = static_cast<int>(static_cast<long long>(part) * t16 / nparts) * 16;
   const int v_hi = min(static_cast<int>(static_cast<long long>(part + 1) * t16 / nparts) * 16, V);
   const int npass = max(v_hi - v_lo, 0) / WROWS + ((max(v_hi - v_lo, 0) % WROWS) != 0);
-  const int nch = hidden / kKC;
+  const int nch = hidden / kKC;          // even: the kernel is served only when hidden % 128 == 0
   const int total = npass * nch;
   const int rot = ((part >> 3) * nch / 32) % nch;
-  unsigned char* const hbase = smem + kWideWStages * WBUF;
 
   // running partials: own tiles (complete over the part) and the remaining
   // tiles (this wave's weight tiles only; merged across waves at the end)
@@ -769,36 +811,36 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     if constexpr (MODE == kModeSample) runx[t] = empty_spartial();
     else runx[t] = empty_partial();
   }
-  // activation row of this lane in each tile it multiplies (own, then the
-  // remaining ones), and its block position (temperature sampling only)
-  int hrow[QR];
+  // activation tile of each tile slot of this wave (own, then the remaining
+  // ones), and its lanes' block positions (temperature sampling only)
+  int htile[QR];
 #pragma unroll
-  for (int t = 0; t < QR; ++t) hrow[t] = (t < Q ? w * Q + t : 4 * Q + t - Q) * 32 + ln;
+  for (int t = 0; t < QR; ++t) htile[t] = t < Q ? w * Q + t : 4 * Q + t - Q;
   unsigned pos[QR];
   if constexpr (MODE == kModeSample) {
 #pragma unroll
     for (int t = 0; t < QR; ++t)
-      pos[t] = static_cast<unsigned>(rows[row0 + min(hrow[t], Mg - 1)] % smp.B);
+      pos[t] = static_cast<unsigned>(rows[row0 + min(htile[t] * 32 + ln, Mg - 1)] % smp.B);
   }
 
   if (total > 0) {
-    // ---- loads: 16-byte pieces straight into LDS, 8 rows per instruction;
-    // instruction p of wave w fills rows 8 (4p + w) .. +8 of a stage, lane
-    // l the XOR-swizzled slot of row 8 (4p + w) + l / 8
+    // ---- the weight: 16-byte pieces straight into LDS, 8 rows per
+    // instruction; instruction p of wave w fills rows 8 (4p + w) .. +8 of a
+    // stage, lane l the XOR-swizzled slot of row 8 (4p + w) + l / 8
     const int r8 = lane >> 3;
     const int ls = (lane & 7) ^ r8 ^ (w & 1);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned short*>(W) + static_cast<size_t>(v_lo) * hidden, 0,
         (v_hi - v_lo) * row_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t hr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
     const int wv = (8 * w + r8) * row_bytes + ls * 16;
-    int hv[TH];
+    // ---- the activation fragments: one 1 KB read each from the
+    // operand-ordered copy (bounds-checked descriptor)
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(Hf), 0, hf_bytes, 0x00020000);
+    int hoff[QR];
 #pragma unroll
-    for (int p = 0; p < TH; ++p)
-      hv[p] = rows[row0 + min(8 * (4 * p + w) + r8, Mg - 1)] * row_bytes + ls * 16;
-    LoadCursor<kWideWStages> lw{0, 0, 0, 0};
-    LoadCursor<kWideHStages> lhc{0, 0, 0, 0};
+    for (int t = 0; t < QR; ++t) hoff[t] = ((row0 >> 5) + htile[t]) * (hidden >> 4) * 1024 + lane * 16;
+    LoadCursor<S> lw{0, 0, 0, 0};
     auto kc_of = [&](int kci) __attribute__((always_inline)) {
       const int kc = kci + rot;
       return kc >= nch ? kc - nch : kc;
@@ -812,42 +854,33 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
                                                  so + 32 * p * row_bytes, 0, kWeightAux);
       lw.step(total, nch);
     };
-    auto issue_h = [&]() __attribute__((always_inline)) {
-      unsigned char* dst = hbase + lhc.stage * HBUF;
-      const int so = kc_of(lhc.kci) * kRB;
-#pragma unroll
-      for (int p = 0; p < TH; ++p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, LOPA_LDS(dst + (4 * p + w) * 1024), 16, hv[p],
-                                                 so, 0, 0);
-      lhc.step(total, nch);
+    // activation fragments of one chunk: [tile slot][K step]
+    using HChunk = u32x4[QR][KS];
+    auto load_h = [&](auto h_c, HChunk& dst, int kc) __attribute__((always_inline)) {
+      constexpr int h = decltype(h_c)::value, j = h / QR, t = h % QR;   // K-step-major
+      dst[t][j] = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff[t] + j * 1024, kc * 4096, 0);
     };
 
-    // ---- fragments of one K step: the weight tiles, the activation tiles
-    // this wave multiplies, and (R > 0) its weight tiles w + 4k paired with
-    // the remaining activation tiles.  They are read one at a time, in the
-    // order the step's MFMAs first use them (WideOrder).
+    // ---- weight fragments of one K step, read one at a time in the order
+    // the step's MFMAs first use them: w0 .. w(TW-1), then the tiles w + 4k
+    // paired with the remaining activation tiles
     struct Frags {
-      u16x8 w[TW], h[QR], xw[XP];
+      u16x8 w[TW], xw[XA];
     };
-    using Ord = WideOrder<TW, Q, R>;
-    // read number k of K step j of the chunk in W stage sw / H stage sh
-    auto read_one = [&](auto k_c, int sw, int sh, int j, Frags& f) __attribute__((always_inline)) {
+    auto read_one = [&](auto k_c, int sw, int j, Frags& f) __attribute__((always_inline)) {
       constexpr int k = decltype(k_c)::value;
-      constexpr int kind = Ord::kind(k), x = Ord::index(k);
       const int sl = 2 * j + lh;   // logical slot: K values 16j + 8lh .. +8
-      if constexpr (kind == 0) {
-        const int r = x * 32 + ln;
-        f.w[x] = *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
-      } else if constexpr (kind == 1) {
-        f.h[x] = *reinterpret_cast<const u16x8*>(hbase + sh * HBUF + hrow[x] * kRB +
-                                                 swz<kKC>(hrow[x], sl) * 16);
+      if constexpr (k < TW) {
+        const int r = k * 32 + ln;
+        f.w[k] = *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
       } else {
-        const int r = (w + 4 * x) * 32 + ln;
-        f.xw[x] = *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
+        const int r = (w + 4 * (k - TW)) * 32 + ln;
+        f.xw[k - TW] =
+            *reinterpret_cast<const u16x8*>(smem + sw * WBUF + r * kRB + swz<kKC>(r, sl) * 16);
       }
     };
 
-    f32x16 acc[Q][TW], accx[R > 0 ? R : 1][XP];
+    f32x16 acc[Q][TW], accx[R > 0 ? R : 1][XA];
 #pragma unroll
     for (int t = 0; t < Q; ++t)
 #pragma unroll
@@ -855,22 +888,23 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
 #pragma unroll
     for (int t = 0; t < (R > 0 ? R : 1); ++t)
 #pragma unroll
-      for (int k = 0; k < XP; ++k) accx[t][k] = f32x16{};
+      for (int k = 0; k < XA; ++k) accx[t][k] = f32x16{};
 
     // NL: live weight tiles of the pass (the others are neither multiplied
     // nor folded); the remaining tiles' pairs always run (a pair past the
     // part reads zeros and its entries are dropped by the masked fold)
-    auto mfma_one = [&](auto nl_c, auto i_c, const Frags& f) __attribute__((always_inline)) {
+    auto mfma_one = [&](auto nl_c, auto i_c, const Frags& f, const HChunk& hc, int j)
+        __attribute__((always_inline)) {
       constexpr int NL = decltype(nl_c)::value, i = decltype(i_c)::value;
       if constexpr (i < Q * NL) {
         constexpr int t = i / NL, n = i % NL;
         acc[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, f.h[t]), acc[t][n], 0,
-            0, 0);
+            __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, hc[t][j]), acc[t][n],
+            0, 0, 0);
       } else {
         constexpr int k = (i - Q * NL) / R, t = (i - Q * NL) % R;
         accx[t][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, f.h[Q + t]),
+            __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, hc[Q + t][j]),
             accx[t][k], 0, 0, 0);
       }
     };
@@ -934,89 +968,92 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
       }
     };
 
-    // ---- prologue: W(0), H(0), W(1); the barrier; H(1), W(2).  At every
-    // barrier the activation chunk is issued before the weight chunk, so
-    // waiting for chunk c + 1 leaves only W(c + 2) in flight.
-    issue_w();
-    issue_h();
-    issue_w();
-    wait_vm_lgkm0<TW>();
-    raw_barrier();
-    issue_h();
-    issue_w();
-    // Fragments are read one K step ahead, one read after each MFMA, so a
-    // read has most of a step's MFMAs to land; the order is pinned with
-    // scheduling barriers (left to itself the compiler sinks the reads next
-    // to their MFMAs and waits on them there).
+    // ---- prologue: W(0) .. W(S - 2), then the activation fragments of
+    // chunk 0; W(0) .. W(S - 4) landed and the barrier; the first K step's
+    // weight fragments.  Steady state: during chunk c's first three K steps
+    // the activation fragments of chunk c + 1 are loaded (into the other
+    // register set), and after the barrier in its last step W(c + S - 1)
+    // goes into the stage chunk c - 1 left; at that barrier W(c + 1) must
+    // have landed, with VM_BAR loads after it still allowed in flight (from
+    // chunk S - 3 on; the earlier chunks' weight has landed in the prologue).
+    // The compiler waits for each activation register itself before its
+    // first MFMA.
     static_assert(KS == 4, "one chunk is four K steps");
-    constexpr int NR = Ord::count;
+    HChunk ha, hb;
+    static_for<S - 1>([&](auto) { issue_w(); });
+    int hci = 0;   // chunk index (within the pass) of the activation loads
+    static_for<NH>([&](auto h) { load_h(h, ha, kc_of(0)); });
+    wait_vm_lgkm0<2 * TW + NH>();
+    raw_barrier();
     Frags f0, f1;
-    int cw = 0, chs = 0;   // stages of the chunk being computed
-    static_for<NR>([&](auto k) { read_one(k, cw, chs, 0, f0); });
-    // K step j (0..2) of the chunk: its MFMAs from cur, step j + 1 read into nxt
-    auto step = [&](auto nl_c, const Frags& cur, Frags& nxt, int j) __attribute__((always_inline)) {
+    int cw = 0;   // stage of the chunk being computed
+    static_for<NR>([&](auto k) { read_one(k, cw, 0, f0); });
+    // K step j (0..2) of the chunk: its MFMAs from fc and hc, step j + 1's
+    // weight reads into fn, and a share of the next chunk's activation loads
+    auto step = [&](auto nl_c, const Frags& fc, Frags& fn, const HChunk& hc, HChunk& hn, int kcn,
+                    auto j_c) __attribute__((always_inline)) {
       constexpr int NM = Q * decltype(nl_c)::value + R * XP;
-      static_for<(NM > NR ? NM : NR)>([&](auto i) {
+      constexpr int NSL = NM > NR ? NM : NR;
+      constexpr int J = decltype(j_c)::value;
+      static_for<NSL>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        if constexpr (I < NM) mfma_one(nl_c, i, cur);
-        if constexpr (I < NR) read_one(i, cw, chs, j + 1, nxt);
+        if constexpr (I < NM) mfma_one(nl_c, i, fc, hc, J);
+        if constexpr (I < NR) read_one(i, cw, J + 1, fn);
+        // activation loads h_lo(g) .. h_lo(g + 1) - 1 go to slot g of the
+        // three steps, h_lo(g) = ceil(g NH / 3 NSL): every load exactly once,
+        // spread evenly (several per slot in a short last pass)
+        constexpr int g = J * NSL + I;
+        constexpr int h_lo = (g * NH + 3 * NSL - 1) / (3 * NSL);
+        constexpr int h_hi = ((g + 1) * NH + 3 * NSL - 1) / (3 * NSL);
+        static_for<(NH + 3 * NSL - 1) / (3 * NSL)>([&](auto q) {
+          constexpr int h = h_lo + decltype(q)::value;
+          if constexpr (h < h_hi) load_h(std::integral_constant<int, h>{}, hn, kcn);
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // One chunk.  Step 3 takes the barrier after its first PRE MFMAs: this
-    // wave's loads of chunk c + 1 have landed and its reads of chunk c are
-    // done (the last were issued during step 2), and after the barrier every
-    // wave's are; the chunk's stages then take H(c + 2) and W(c + 3), and the
-    // step's other MFMAs cover the reads of the next chunk's step 0.  (After
-    // the last chunk this loads the last chunk again and reads stages that
-    // are not used: every wave takes the same steps.)
-    auto chunk = [&](auto nl_c) __attribute__((always_inline)) {
+    auto chunk = [&](auto nl_c, const HChunk& hc, HChunk& hn) __attribute__((always_inline)) {
       constexpr int NM = Q * decltype(nl_c)::value + R * XP;
       constexpr int PRE = NM - NR > 2 ? NM - NR : (NM < 2 ? NM : 2);
-      step(nl_c, f0, f1, 0);
-      step(nl_c, f1, f0, 1);
-      step(nl_c, f0, f1, 2);
+      hci = hci + 1 == nch ? 0 : hci + 1;
+      const int kcn = kc_of(hci);
+      step(nl_c, f0, f1, hc, hn, kcn, std::integral_constant<int, 0>{});
+      step(nl_c, f1, f0, hc, hn, kcn, std::integral_constant<int, 1>{});
+      step(nl_c, f0, f1, hc, hn, kcn, std::integral_constant<int, 2>{});
       static_for<PRE>([&](auto i) {
-        mfma_one(nl_c, i, f1);
+        mfma_one(nl_c, i, f1, hc, 3);
         __builtin_amdgcn_sched_barrier(0);
       });
-      wait_vm_lgkm0<TW>();
+      asm volatile("" ::: "memory");
+      wait_vm_lgkm0<VM_BAR>();
       raw_barrier();
-      // the loads of H(c + 2), then W(c + 3), two after each MFMA
-      unsigned char* const hdst = hbase + lhc.stage * HBUF;
-      const int hso = kc_of(lhc.kci) * kRB;
+      // W(c + S - 1) into the stage chunk c - 1 left, spread over the step's
+      // remaining MFMAs, with the reads of the next chunk's first step
       unsigned char* const wdst = smem + lw.stage * WBUF;
       const int wso = lw.pass * WROWS * row_bytes + kc_of(lw.kci) * kRB;
-      lhc.step(total, nch);
       lw.step(total, nch);
-      auto load_one = [&](auto k_c) __attribute__((always_inline)) {
-        constexpr int k = decltype(k_c)::value;
-        if constexpr (k < TH)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, LOPA_LDS(hdst + (4 * k + w) * 1024), 16,
-                                                   hv[k], hso, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              wr, LOPA_LDS(wdst + (4 * (k - TH) + w) * 1024), 16, wv,
-              wso + 32 * (k - TH) * row_bytes, 0, kWeightAux);
-      };
-      cw = cw + 1 == kWideWStages ? 0 : cw + 1;
-      chs = chs + 1 == kWideHStages ? 0 : chs + 1;
+      cw = cw + 1 == S ? 0 : cw + 1;
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int NLD = TH + TW, NSLOT = NM - PRE > NR ? NM - PRE : NR;
-      constexpr int LPS = (NLD + NSLOT - 1) / NSLOT;   // loads per slot
+      constexpr int NSLOT = NM - PRE > NR ? NM - PRE : NR;
+      constexpr int LPS = (TW + NSLOT - 1) / NSLOT;   // loads per slot
       static_for<NSLOT>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        if constexpr (I < NM - PRE) mfma_one(nl_c, std::integral_constant<int, PRE + I>{}, f1);
+        if constexpr (I < NM - PRE) mfma_one(nl_c, std::integral_constant<int, PRE + I>{}, f1, hc, 3);
         static_for<LPS>([&](auto q) {
-          constexpr int k = I * LPS + decltype(q)::value;
-          if constexpr (k < NLD) load_one(std::integral_constant<int, k>{});
+          constexpr int p = I * LPS + decltype(q)::value;
+          if constexpr (p < TW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(wdst + (4 * p + w) * 1024), 16,
+                                                     wv, wso + 32 * p * row_bytes, 0, kWeightAux);
         });
-        if constexpr (I < NR) read_one(i, cw, chs, 0, f0);
+        if constexpr (I < NR) read_one(i, cw, 0, f0);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
     auto run_pass = [&](auto nl_c, auto masked_c, int pass) __attribute__((always_inline)) {
-      for (int kk = 0; kk < nch; ++kk) chunk(nl_c);
+      for (int kk = 0; kk < nch; kk += 2) {
+        chunk(nl_c, ha, hb);
+        chunk(nl_c, hb, ha);
+      }
       fold(nl_c, masked_c, pass);
     };
     for (int pass = 0; pass + 1 < npass; ++pass)
@@ -1099,8 +1136,8 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
 // narrow kernel serves the row count.
 template <int MODE>
 __global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int h_bytes,
-              const unsigned short* __restrict__ H, const unsigned short* __restrict__ W,
+k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int hf_bytes,
+              const unsigned short* __restrict__ Hf, const unsigned short* __restrict__ W,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
               float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
@@ -1116,11 +1153,15 @@ k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int h_bytes,
   const int row0 = group * g.th * 32;
   if (part >= g.nparts || row0 >= M) return;
   const int Mg = min(M - row0, g.th * 32);
-#define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, h_bytes, H, W, rows, smem, ws_m, ws_s, ws_i, \
-                  ws_t, ws_z, smp
+#define LOPA_ARGS V, hidden, g.nparts, part, Mg, row0, hf_bytes, Hf, W, rows, smem, ws_m, ws_s, \
+                  ws_i, ws_t, ws_z, smp
   switch (g.th) {   // the layouts wide_takes() can reach
     case 6: wide_body<8, 1, 2, MODE>(LOPA_ARGS); break;
+    case 7: wide_body<8, 1, 3, MODE>(LOPA_ARGS); break;
     case 9: wide_body<4, 2, 1, MODE>(LOPA_ARGS); break;
+    case 10: wide_body<4, 2, 2, MODE>(LOPA_ARGS); break;
+    case 11: wide_body<4, 2, 3, MODE>(LOPA_ARGS); break;
+    case 12: wide_body<4, 3, 0, MODE>(LOPA_ARGS); break;
     default: wide_body<4, 3, 1, MODE>(LOPA_ARGS); break;
   }
 #undef LOPA_ARGS
@@ -1341,8 +1382,7 @@ k_lmhead_merge(int V, int ntiles, int mfma, int nb_max, int m_max,
 // confidence and entropy modes, no full logits requested).
 template <int MODE>
 static bool wide_serves(const lopa::HeadPlan& p, int hidden, const float* logits_out) {
-  (void)hidden;
-  return MODE != lopa::kModeSample && p.mfma && (p.m_max + 31) / 32 >= lopa::kWideMinTiles &&
+  return MODE != lopa::kModeSample && p.mfma && lopa::wide_possible(p.m_max, hidden) &&
          logits_out == nullptr;
 }
 
@@ -1387,10 +1427,20 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
                        wm, wsum, wi, wt, wz, smp, logits_out);
     LOPA_LAUNCH_CHECK();
     if constexpr (MODE != kModeSample) {
-      if (wide)
+      if (wide) {
+        // the activation rows in operand order, after the partial planes
+        const size_t hf_off = (5 * plane * 4 + 255) / 256 * 256;
+        unsigned short* hf = reinterpret_cast<unsigned short*>(static_cast<char*>(ws) + hf_off);
+        const size_t hfb = hfrag_bytes(p.m_max, hidden);
+        const int nfrag = (p.m_max + 31) / 32 * (hidden / 16);
+        hipLaunchKernelGGL(k_lmhead_hfrag, dim3((nfrag + 3) / 4), dim3(256), 0, stream, hidden,
+                           nb_max, p.m_max, h_bytes, Hb, rows, row_ptr, nb,
+                           reinterpret_cast<u32x4*>(hf));
+        LOPA_LAUNCH_CHECK();
         hipLaunchKernelGGL(k_lmhead_wide<MODE>, dim3(kHeadParts), dim3(kWideThreads), 0, stream,
-                           V, hidden, nb_max, p.m_max, h_bytes, Hb, Wb, rows, row_ptr, nb, wm,
-                           wsum, wi, wt, wz, smp);
+                           V, hidden, nb_max, p.m_max, static_cast<int>(hfb), hf, Wb, rows,
+                           row_ptr, nb, wm, wsum, wi, wt, wz, smp);
+      }
     }
   } else {
     const dim3 grid(p.ntiles, p.m_max);
@@ -1450,9 +1500,12 @@ extern "C" int lopa_lmhead_sample(const lopa_dims* dims, float temperature, uint
 // live in a fixed device array instead of a caller workspace.
 // ---------------------------------------------------------------------------
 
-// 5 MiB: every bfloat16 MFMA shape (m_max <= 1024 rows x 256 vocabulary parts
-// x 20 bytes) fits; the float32 path fits while m_max x ceil(V / 256) <= 262144.
-constexpr size_t kScratchBytes = static_cast<size_t>(5) << 20;
+// 16 MiB: the partials of every bfloat16 MFMA shape (m_max <= 1024 rows x 256
+// vocabulary parts x 20 bytes = 5 MiB) plus the wide kernel's operand-ordered
+// activation copy while m_max (rounded up to 32) x hidden x 2 bytes <= 11 MiB
+// (1024 rows at hidden 5632); the float32 path fits while
+// m_max x ceil(V / 256) <= 838860.
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {

@@ -116,8 +116,11 @@ def test_workspace_size_and_shortfall():
     # = 72 workgroups: 3 splits (3 units + the merge's 5 < 9) of attention
     # partials (O, max, sum = 130 floats per row), which dominate
     assert need == 3 * 4 * (5 * 32 * 7) * 130 * 4
-    # 9 branches: 128 workgroups leave room for 2 splits, which would not pay
-    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 20
+    # 9 branches: 128 workgroups leave room for 2 splits, which would not pay;
+    # the LM head's 288 rows (9 tiles) may reach the wide kernel, which also
+    # takes the operand-ordered copy of the rows (288 x hidden bf16) after
+    # the partials
+    assert lopa.workspace_bytes(_dims(k_max=8)) == 9 * 32 * 256 * 20 + 9 * 32 * 3584 * 2
     # prefix 4096 takes the 128-row kernel: 32 row groups x 4 heads = 128
     # workgroups -> 2 splits (33 units + the merge's 8 < 65)
     assert lopa.workspace_bytes(_dims(L=4096, B=64, k_max=8)) == 2 * 4 * (9 * 64 * 7) * 130 * 4
@@ -248,14 +251,19 @@ def test_model_slot_table_overflow_rejected():
 
 def test_noalloc_head_rejects_before_any_launch():
     """The allocation-free LM head checks its arguments, and that its partials
-    fit the library's fixed 5 MiB array, before touching the HIP runtime."""
+    fit the library's fixed 16 MiB array, before touching the HIP runtime."""
     L = lopa.lib()
     fake = ctypes.c_void_p(256)
     d = _dims()
     assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), None, *([fake] * 7), None) == -1
     assert L.lopa_lmhead_conf_noalloc(None, *([fake] * 8), None) == -1
-    # float32 path over a 152064-entry vocabulary with 16 x 64 rows: 1024 x 594
-    # partials of 20 bytes (12 MB) do not fit
-    d = _dims(dtype=lopa.F32, B=64, k_max=15)
+    # float32 path over a 400000-entry vocabulary with 16 x 64 rows: 1024 x 1563
+    # partials of 20 bytes (32 MB) do not fit
+    d = _dims(dtype=lopa.F32, V=400000, B=64, k_max=15)
+    assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), *([fake] * 8), None) == -5
+    # bfloat16 at hidden 28 x 256 with 1024 rows: 5 MiB of partials plus the
+    # wide kernel's 14 MiB copy of the rows do not fit
+    d = _dims(d=256, B=64, k_max=15)
+    assert lopa.workspace_bytes(d) == 1024 * 256 * 20 + 1024 * 7168 * 2
     assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), *([fake] * 8), None) == -5
     assert "scratch" in lopa.status_string(-5)

@@ -343,32 +343,44 @@ def test_gpu_lmhead(name, ov, _):
     np.testing.assert_allclose(lg, ref.logits, rtol=1e-5, atol=1e-5 * np.abs(ref.logits).max())
 
 
-# Without full logits, m_max of 6 row tiles or more: the wide kernel (four
-# waves, register tiles of q owned row tiles plus a share of the r remaining
-# ones) where it serves the row-tile count (6, 9, 13, 17, 18), the narrow one
-# elsewhere (and alone when m_max is at most 5 tiles).  Row groups of
-# th = 4q + r tiles, 8 weight tiles per pass up to 7 row tiles, 4 from 8; vocabulary parts with empty parts (V < 4096), a last
-# pass of 1 .. all live weight tiles, a vocabulary size that is not a
-# multiple of 16, and 2 and 3 row groups.  Rows: every masked position of
-# every branch slot.
+# Without full logits, m_max of 6 row tiles or more and hidden a multiple of
+# 128: the wide kernel (four waves, register tiles of q owned row tiles plus
+# a share of the r remaining ones, activation fragments loaded into
+# registers from the operand-ordered copy) where it serves the row-tile count
+# (6, 9-14, 17-20, 23-26), the narrow one elsewhere (and alone when m_max is
+# at most 5 tiles or hidden is not a multiple of 128).  Row groups of
+# th = 4q + r tiles, 8 weight tiles per pass up to 7 row tiles, 4 from 8;
+# vocabulary parts with empty parts (V < 4096), a last pass of 1 .. all live
+# weight tiles (with 2 and with 4 K chunks: the activation register sets
+# alternate by chunk), a vocabulary size that is not a multiple of 16, and 2
+# and 3 row groups.  Rows: every masked position of every branch slot.
 WIDE_CASES = [
     # name, overrides (M = (k + 1) m)
     ("tiles5-narrow-alone", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=3000, B=32, m=30, k=4)),
     ("th6-empty-parts", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=3000, B=48, m=45, k=3)),
     ("th6-tw8", dict(dtype="bf16", Hq=2, Hkv=2, d=64, V=9000, B=60, m=60, k=2)),
     ("th6-tw8-last-5", dict(dtype="bf16", Hq=2, Hkv=2, d=64, V=37100, B=60, m=60, k=2)),
-    ("th7-tw8-two-passes", dict(dtype="bf16", Hq=1, Hkv=1, d=128, V=65636, B=56, m=56, k=3)),
-    ("th7-tw8-last-7", dict(dtype="bf16", Hq=1, Hkv=1, d=128, V=50000, B=56, m=56, k=3)),
-    ("th8-tw4-one-pass", dict(dtype="bf16", Hq=2, Hkv=1, d=128, V=20000, B=32, m=30, k=7)),
+    ("tiles7-narrow", dict(dtype="bf16", Hq=1, Hkv=1, d=128, V=65636, B=56, m=56, k=3)),
+    ("tiles8-narrow", dict(dtype="bf16", Hq=2, Hkv=1, d=128, V=20000, B=32, m=30, k=7)),
     ("th9-ragged-V", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=33333, B=32, m=32, k=8)),
     ("th10", dict(dtype="bf16", Hq=4, Hkv=1, d=64, V=12000, B=64, m=64, k=4)),
-    ("th11", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=100000, B=64, m=50, k=6)),
-    ("th12-hidden192", dict(dtype="bf16", Hq=3, Hkv=1, d=64, V=70000, B=64, m=48, k=7)),
+    ("th11", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=100000, B=64, m=50, k=6)),
+    ("th11-hidden64-narrow", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=100000, B=64, m=50, k=6)),
+    ("th12-tw4", dict(dtype="bf16", Hq=4, Hkv=1, d=64, V=70000, B=64, m=48, k=7)),
+    ("th12-hidden192-narrow", dict(dtype="bf16", Hq=3, Hkv=1, d=64, V=70000, B=64, m=48, k=7)),
     ("th13-last-pass-1-tile", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=40000, B=32, m=26, k=15)),
-    ("two-groups-th8", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=7000, B=50, m=50, k=8)),
+    ("th13-4-chunks-last-pass-1-tile",
+     dict(dtype="bf16", Hq=4, Hkv=1, d=64, V=40000, B=32, m=26, k=15)),
+    ("tiles14-two-groups-th7", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9000, B=64, m=56, k=7)),
+    ("tiles14-th7-two-passes-last-7",
+     dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=59392, B=64, m=56, k=7)),
+    ("tiles15-narrow", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=7000, B=50, m=50, k=8)),
     ("tiles17-two-groups-th9", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=21000, B=60, m=60, k=8)),
     ("tiles18-two-groups-th9", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9100, B=64, m=57, k=9)),
-    ("three-groups-th11", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=5000, B=64, m=64, k=15)),
+    ("tiles24-two-groups-th12", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9000, B=64, m=48, k=15)),
+    ("tiles26-two-groups-th13-last-1",
+     dict(dtype="bf16", Hq=4, Hkv=1, d=64, V=20000, B=64, m=52, k=15)),
+    ("tiles32-narrow-three-groups", dict(dtype="bf16", Hq=1, Hkv=1, d=64, V=5000, B=64, m=64, k=15)),
 ]
 
 

@@ -40,6 +40,8 @@ SHAPES = [
     # name, dims, rows of the first call, rows of the second call
     ("bf16-wide-then-narrow", dict(L=0, B=64, Hq=2, Hkv=1, d=128, V=9000, k_max=15, dtype=lopa.BF16),
      415, 100),
+    ("bf16-wide-twice", dict(L=0, B=64, Hq=2, Hkv=1, d=128, V=9000, k_max=15, dtype=lopa.BF16),
+     540, 300),
     ("bf16-narrow-three-groups", dict(L=0, B=64, Hq=2, Hkv=1, d=64, V=30000, k_max=15,
                                       dtype=lopa.BF16), 700, 37),
     ("f32-plain", dict(L=0, B=32, Hq=2, Hkv=2, d=32, V=5000, k_max=3, dtype=lopa.F32), 120, 9),
