@@ -782,9 +782,13 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
   // chunk it waits for come the activation loads of S - 2 chunks and S - 3
   // weight chunks (the issue order of the loop below)
   constexpr int VM_BAR = (S - 3) * TW + (S - 2) * NH;
+  // activation loads run LA K steps ahead, in a ring of eight register sets
+  // (LA + 1 of them live: as many as keep the layout free of scratch spills)
+  constexpr int LA = QR * 4 + NR * 2 <= 22 ? 7 : QR * 4 + NR * 2 <= 26 ? 5 : 4;
   static_assert(TW % 4 == 0 && Q >= 1 && R >= 0 && R < 4 && TH <= kWideMaxTiles, "wide layout");
   static_assert(S >= 4 && S * WBUF <= kWideSmem, "wide LDS");
-  static_assert(VM_BAR < 64 && 2 * TW + NH < 64, "vmcnt range");
+  static_assert(VM_BAR < 64 && 2 * TW + LA * QR < 64, "vmcnt range");
+  static_assert(LA >= 4 && LA <= 7, "activation ring");
   static_assert(R * 4 * 32 * static_cast<int>(sizeof(RP)) <= kWideSmem, "merge area");
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -854,11 +858,13 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
                                                  so + 32 * p * row_bytes, 0, kWeightAux);
       lw.step(total, nch);
     };
-    // activation fragments of one chunk: [tile slot][K step]
-    using HChunk = u32x4[QR][KS];
-    auto load_h = [&](auto h_c, HChunk& dst, int kc) __attribute__((always_inline)) {
-      constexpr int h = decltype(h_c)::value, j = h / QR, t = h % QR;   // K-step-major
-      dst[t][j] = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff[t] + j * 1024, kc * 4096, 0);
+    // activation fragments of one K step, by tile slot; the registers hold
+    // a ring of eight K steps (step j of the first or second chunk of a pair
+    // in set j or 4 + j)
+    using HStep = u32x4[QR];
+    auto load_h = [&](auto t_c, HStep& dst, int kc, int j) __attribute__((always_inline)) {
+      constexpr int t = decltype(t_c)::value;
+      dst[t] = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff[t] + j * 1024, kc * 4096, 0);
     };
 
     // ---- weight fragments of one K step, read one at a time in the order
@@ -893,18 +899,18 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     // NL: live weight tiles of the pass (the others are neither multiplied
     // nor folded); the remaining tiles' pairs always run (a pair past the
     // part reads zeros and its entries are dropped by the masked fold)
-    auto mfma_one = [&](auto nl_c, auto i_c, const Frags& f, const HChunk& hc, int j)
+    auto mfma_one = [&](auto nl_c, auto i_c, const Frags& f, const HStep& hc)
         __attribute__((always_inline)) {
       constexpr int NL = decltype(nl_c)::value, i = decltype(i_c)::value;
       if constexpr (i < Q * NL) {
         constexpr int t = i / NL, n = i % NL;
         acc[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, hc[t][j]), acc[t][n],
+            __builtin_bit_cast(bf16x8, f.w[n]), __builtin_bit_cast(bf16x8, hc[t]), acc[t][n],
             0, 0, 0);
       } else {
         constexpr int k = (i - Q * NL) / R, t = (i - Q * NL) % R;
         accx[t][k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, hc[Q + t][j]),
+            __builtin_bit_cast(bf16x8, f.xw[k]), __builtin_bit_cast(bf16x8, hc[Q + t]),
             accx[t][k], 0, 0, 0);
       }
     };
@@ -968,60 +974,84 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
       }
     };
 
-    // ---- prologue: W(0) .. W(S - 2), then the activation fragments of
-    // chunk 0; W(0) .. W(S - 4) landed and the barrier; the first K step's
-    // weight fragments.  Steady state: during chunk c's first three K steps
-    // the activation fragments of chunk c + 1 are loaded (into the other
-    // register set), and after the barrier in its last step W(c + S - 1)
-    // goes into the stage chunk c - 1 left; at that barrier W(c + 1) must
+    // ---- prologue: W(0) .. W(S - 2), then the activation fragments of K
+    // steps 0 .. LA - 1; W(0) .. W(S - 4) landed and the barrier; the first
+    // K step's weight fragments.  Steady state: during K step s the
+    // activation fragments of step s + LA are loaded into a free set of the
+    // ring (steps 0..2 of a chunk: spread over their MFMAs; step 3: before its
+    // barrier), and after the barrier in the chunk's last step W(c + S - 1)
+    // goes into the stage chunk c - 1 left.  At that barrier W(c + 1) must
     // have landed, with VM_BAR loads after it still allowed in flight (from
     // chunk S - 3 on; the earlier chunks' weight has landed in the prologue).
-    // The compiler waits for each activation register itself before its
-    // first MFMA.
+    // The counter completes in issue order, so an activation load waits for
+    // every weight load issued before it: issued before the chunk's own
+    // weight loads, each one follows weight loads at least LA + 1 K steps
+    // older than its use.  The compiler waits for each activation register
+    // itself before its first MFMA.
     static_assert(KS == 4, "one chunk is four K steps");
-    HChunk ha, hb;
+    HStep hs[8];
     static_for<S - 1>([&](auto) { issue_w(); });
-    int hci = 0;   // chunk index (within the pass) of the activation loads
-    static_for<NH>([&](auto h) { load_h(h, ha, kc_of(0)); });
-    wait_vm_lgkm0<2 * TW + NH>();
+    int hci = 0;   // chunk index (within the pass) of the chunk being computed
+    {
+      const int kc0 = kc_of(0), kc1 = kc_of(1);   // nch >= 2
+      static_for<LA>([&](auto s_c) {
+        constexpr int st = decltype(s_c)::value;
+        static_for<QR>([&](auto t) { load_h(t, hs[st], st < 4 ? kc0 : kc1, st & 3); });
+      });
+    }
+    wait_vm_lgkm0<2 * TW + LA * QR>();
     raw_barrier();
     Frags f0, f1;
     int cw = 0;   // stage of the chunk being computed
     static_for<NR>([&](auto k) { read_one(k, cw, 0, f0); });
     // K step j (0..2) of the chunk: its MFMAs from fc and hc, step j + 1's
-    // weight reads into fn, and a share of the next chunk's activation loads
-    auto step = [&](auto nl_c, const Frags& fc, Frags& fn, const HChunk& hc, HChunk& hn, int kcn,
-                    auto j_c) __attribute__((always_inline)) {
+    // weight reads into fn, and the activation loads of K step s + LA (step
+    // jl of the chunk with K chunk kcl) into hn, spread over the slots
+    auto step = [&](auto nl_c, const Frags& fc, Frags& fn, const HStep& hc, HStep& hn, int kcl,
+                    int jl, auto j_c) __attribute__((always_inline)) {
       constexpr int NM = Q * decltype(nl_c)::value + R * XP;
       constexpr int NSL = NM > NR ? NM : NR;
       constexpr int J = decltype(j_c)::value;
       static_for<NSL>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        if constexpr (I < NM) mfma_one(nl_c, i, fc, hc, J);
+        if constexpr (I < NM) mfma_one(nl_c, i, fc, hc);
         if constexpr (I < NR) read_one(i, cw, J + 1, fn);
-        // activation loads h_lo(g) .. h_lo(g + 1) - 1 go to slot g of the
-        // three steps, h_lo(g) = ceil(g NH / 3 NSL): every load exactly once,
-        // spread evenly (several per slot in a short last pass)
-        constexpr int g = J * NSL + I;
-        constexpr int h_lo = (g * NH + 3 * NSL - 1) / (3 * NSL);
-        constexpr int h_hi = ((g + 1) * NH + 3 * NSL - 1) / (3 * NSL);
-        static_for<(NH + 3 * NSL - 1) / (3 * NSL)>([&](auto q) {
-          constexpr int h = h_lo + decltype(q)::value;
-          if constexpr (h < h_hi) load_h(std::integral_constant<int, h>{}, hn, kcn);
+        // loads ceil(I QR / NSL) .. ceil((I + 1) QR / NSL) - 1 in slot I
+        constexpr int t_lo = (I * QR + NSL - 1) / NSL, t_hi = ((I + 1) * QR + NSL - 1) / NSL;
+        static_for<(QR + NSL - 1) / NSL>([&](auto q) {
+          constexpr int t = t_lo + decltype(q)::value;
+          if constexpr (t < t_hi) load_h(std::integral_constant<int, t>{}, hn, kcl, jl);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    auto chunk = [&](auto nl_c, const HChunk& hc, HChunk& hn) __attribute__((always_inline)) {
+    // chunk P (0 or 1) of a pair: K steps 4P .. 4P + 3 of the ring
+    auto chunk = [&](auto nl_c, auto p_c) __attribute__((always_inline)) {
       constexpr int NM = Q * decltype(nl_c)::value + R * XP;
       constexpr int PRE = NM - NR > 2 ? NM - NR : (NM < 2 ? NM : 2);
-      hci = hci + 1 == nch ? 0 : hci + 1;
-      const int kcn = kc_of(hci);
-      step(nl_c, f0, f1, hc, hn, kcn, std::integral_constant<int, 0>{});
-      step(nl_c, f1, f0, hc, hn, kcn, std::integral_constant<int, 1>{});
-      step(nl_c, f0, f1, hc, hn, kcn, std::integral_constant<int, 2>{});
+      constexpr int B0 = 4 * decltype(p_c)::value;
+      // the chunk 1 and 2 ahead: K chunks of the activation loads
+      const int kca[2] = {kc_of(hci + 1 == nch ? 0 : hci + 1),
+                          kc_of(hci + 2 >= nch ? hci + 2 - nch : hci + 2)};
+      // K step j's load: step (j + LA) % 4 of chunk c + (j + LA) / 4, set (B0 + j + LA) % 8
+      step(nl_c, f0, f1, hs[B0], hs[(B0 + LA) & 7], kca[LA / 4 - 1], LA & 3,
+           std::integral_constant<int, 0>{});
+      step(nl_c, f1, f0, hs[B0 + 1], hs[(B0 + 1 + LA) & 7], kca[(1 + LA) / 4 - 1], (1 + LA) & 3,
+           std::integral_constant<int, 1>{});
+      step(nl_c, f0, f1, hs[B0 + 2], hs[(B0 + 2 + LA) & 7], kca[(2 + LA) / 4 - 1], (2 + LA) & 3,
+           std::integral_constant<int, 2>{});
+      // step 3: its first PRE MFMAs with the activation loads of step s + LA
+      // (before this chunk's weight loads), the barrier, the rest
       static_for<PRE>([&](auto i) {
-        mfma_one(nl_c, i, f1, hc, 3);
+        constexpr int I = decltype(i)::value;
+        mfma_one(nl_c, i, f1, hs[B0 + 3]);
+        constexpr int t_lo = (I * QR + PRE - 1) / PRE, t_hi = ((I + 1) * QR + PRE - 1) / PRE;
+        static_for<(QR + PRE - 1) / PRE>([&](auto q) {
+          constexpr int t = t_lo + decltype(q)::value;
+          if constexpr (t < t_hi)
+            load_h(std::integral_constant<int, t>{}, hs[(B0 + 3 + LA) & 7], kca[(3 + LA) / 4 - 1],
+                   (3 + LA) & 3);
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
       asm volatile("" ::: "memory");
@@ -1033,12 +1063,14 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
       const int wso = lw.pass * WROWS * row_bytes + kc_of(lw.kci) * kRB;
       lw.step(total, nch);
       cw = cw + 1 == S ? 0 : cw + 1;
+      hci = hci + 1 == nch ? 0 : hci + 1;
       __builtin_amdgcn_sched_barrier(0);
       constexpr int NSLOT = NM - PRE > NR ? NM - PRE : NR;
       constexpr int LPS = (TW + NSLOT - 1) / NSLOT;   // loads per slot
       static_for<NSLOT>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        if constexpr (I < NM - PRE) mfma_one(nl_c, std::integral_constant<int, PRE + I>{}, f1, hc, 3);
+        if constexpr (I < NM - PRE)
+          mfma_one(nl_c, std::integral_constant<int, PRE + I>{}, f1, hs[B0 + 3]);
         static_for<LPS>([&](auto q) {
           constexpr int p = I * LPS + decltype(q)::value;
           if constexpr (p < TW)
@@ -1051,8 +1083,8 @@ __device__ __forceinline__ void wide_body(int V, int hidden, int nparts, int par
     };
     auto run_pass = [&](auto nl_c, auto masked_c, int pass) __attribute__((always_inline)) {
       for (int kk = 0; kk < nch; kk += 2) {
-        chunk(nl_c, ha, hb);
-        chunk(nl_c, hb, ha);
+        chunk(nl_c, std::integral_constant<int, 0>{});
+        chunk(nl_c, std::integral_constant<int, 1>{});
       }
       fold(nl_c, masked_c, pass);
     };
