@@ -75,14 +75,14 @@ __host__ __device__ inline HeadGroups head_groups(int M) {
 // wave owns q tiles against every weight tile of a pass, and the r remaining
 // tiles are shared out by weight tile (wave w takes weight tiles w, w + 4,
 // ...), so every wave runs the same number of MFMAs.  tw: weight tiles per
-// pass (8 up to 7 row tiles, else 4).  The weight streams through an LDS
+// pass (8 up to 8 row tiles, else 4).  The weight streams through an LDS
 // ring; the activation fragments go straight from an operand-ordered copy
 // (made per call) into registers.  It serves the row-tile counts where it
 // measured faster than the narrow kernel (k_lmhead_mfma) in a same-box
-// comparison at the 7B shapes (6 and 9..32 tiles): 6, 9-14, 17-20 and 23-26
-// tiles (by 3-20 %; 19, 23 and 25 by their layouts' neighbours); the narrow
-// kernel serves every other count (at 7, 8, 15, 16, 22 and 27-32 tiles it
-// measured equal or up to 12 % faster).  At 5 tiles the wide kernel measured
+// comparison at the 7B shapes (6 and 9..32 tiles): 6, 9-20 and 23-26 tiles
+// (by 3-20 %; 19, 23 and 25 by their layouts' neighbours); the narrow kernel
+// serves every other count (at 7, 8, 22 and 27-32 tiles it measured equal or
+// up to 12 % faster).  At 5 tiles the wide kernel measured
 // 17 % faster as well, but the row count lives on the device, so a call that
 // may reach the wide kernel launches both and the idle one costs about 5 us:
 // a call of at most 5 tiles (block 32, 5 branches: m_max = 160) launches the
@@ -98,13 +98,12 @@ __host__ __device__ inline WideGroups wide_groups(int M) {
   const int tiles = (M + 31) / 32;
   const int g = (tiles + kWideMaxTiles - 1) / kWideMaxTiles;
   const int th = (tiles + g - 1) / g;
-  return WideGroups{th <= 7 ? 8 : 4, th, g, 8 * (kHeadParts / 8 / g)};
+  return WideGroups{th <= 8 ? 8 : 4, th, g, 8 * (kHeadParts / 8 / g)};
 }
 
 __host__ __device__ inline bool wide_takes(int M) {
   const int t = (M + 31) / 32;
-  return t == 6 || (t >= 9 && t <= 14) || (t >= 17 && t <= 20) || t == 23 || t == 24 ||
-         t == 25 || t == 26;
+  return t == 6 || (t >= 9 && t <= 20) || t == 23 || t == 24 || t == 25 || t == 26;
 }
 
 // Whether a call with m_max rows may reach the wide kernel (its K loop takes

@@ -1190,6 +1190,7 @@ k_lmhead_wide(int V, int hidden, int nb_max, int m_max, int hf_bytes,
   switch (g.th) {   // the layouts wide_takes() can reach
     case 6: wide_body<8, 1, 2, MODE>(LOPA_ARGS); break;
     case 7: wide_body<8, 1, 3, MODE>(LOPA_ARGS); break;
+    case 8: wide_body<8, 2, 0, MODE>(LOPA_ARGS); break;
     case 9: wide_body<4, 2, 1, MODE>(LOPA_ARGS); break;
     case 10: wide_body<4, 2, 2, MODE>(LOPA_ARGS); break;
     case 11: wide_body<4, 2, 3, MODE>(LOPA_ARGS); break;

@@ -347,9 +347,9 @@ def test_gpu_lmhead(name, ov, _):
 # 128: the wide kernel (four waves, register tiles of q owned row tiles plus
 # a share of the r remaining ones, activation fragments loaded into
 # registers from the operand-ordered copy) where it serves the row-tile count
-# (6, 9-14, 17-20, 23-26), the narrow one elsewhere (and alone when m_max is
+# (6, 9-20, 23-26), the narrow one elsewhere (and alone when m_max is
 # at most 5 tiles or hidden is not a multiple of 128).  Row groups of
-# th = 4q + r tiles, 8 weight tiles per pass up to 7 row tiles, 4 from 8;
+# th = 4q + r tiles, 8 weight tiles per pass up to 8 row tiles, 4 from 9;
 # vocabulary parts with empty parts (V < 4096), a last pass of 1 .. all live
 # weight tiles (with 2 and with 4 K chunks: the activation register sets
 # alternate by chunk), a vocabulary size that is not a multiple of 16, and 2
@@ -374,7 +374,9 @@ WIDE_CASES = [
     ("tiles14-two-groups-th7", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9000, B=64, m=56, k=7)),
     ("tiles14-th7-two-passes-last-7",
      dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=59392, B=64, m=56, k=7)),
-    ("tiles15-narrow", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=7000, B=50, m=50, k=8)),
+    ("tiles15-two-groups-th8-tw8", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=7000, B=50, m=50, k=8)),
+    ("tiles16-th8-tw8-last-1",
+     dict(dtype="bf16", Hq=4, Hkv=1, d=64, V=35840, B=64, m=32, k=15)),
     ("tiles17-two-groups-th9", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=21000, B=60, m=60, k=8)),
     ("tiles18-two-groups-th9", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9100, B=64, m=57, k=9)),
     ("tiles24-two-groups-th12", dict(dtype="bf16", Hq=2, Hkv=1, d=64, V=9000, B=64, m=48, k=15)),
