@@ -40,10 +40,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 HEAD_SOURCES = ("lmhead.hip", "head_plan.hpp", "stream_tile.hpp", "lopa_common.hpp")
 ATTN_SOURCES = ("attn.hip", "attn_plan.hpp", "lopa_common.hpp")
 HEAD_TRAFFIC = {
-    "7b-bf16-L512-B32-m24-k4": ("8901b5135d8cece7", 1104645705),
-    "7b-bf16-L2048-B32-m28-k8": ("8901b5135d8cece7", 1111052472),
-    "7b-bf16-L1024-B32-m24-k15": ("8901b5135d8cece7", 1131197159),
-    "7b-bf16-L4096-B64-m48-k8": ("8901b5135d8cece7", 1136714310),
+    "7b-bf16-L512-B32-m24-k4": ("f87d9b2fcb95d115", 1104605110),
+    "7b-bf16-L2048-B32-m28-k8": ("f87d9b2fcb95d115", 1111029384),
+    "7b-bf16-L1024-B32-m24-k15": ("f87d9b2fcb95d115", 1131285813),
+    "7b-bf16-L4096-B64-m48-k8": ("f87d9b2fcb95d115", 1136938159),
 }
 ATTN_TRAFFIC = {
     "7b-bf16-L512-B32-m24-k4": ("b83e9d0f5e96b081", 26936320),
