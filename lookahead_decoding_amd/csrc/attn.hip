@@ -752,8 +752,9 @@ k_attn_wide(int L, int B, int Hq, int Hkv, int nb_max, int row_groups, int split
 }
 
 // Merge of the splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// rounded to bf16.  One wave per row (2 dims per lane); every split's loads
-// are issued before any is used, so the merge costs one memory round trip.
+// rounded to bf16.  Half a wave per row (4 dims per lane, 16-byte loads),
+// eight rows per workgroup; every split's loads are issued before any is
+// used, so the merge costs one memory round trip.
 template <int S>
 __global__ void __launch_bounds__(256)
 k_attn_combine(int B, int Hq, int Hkv, int nb_max, const int32_t* __restrict__ nb_ptr,
@@ -763,38 +764,40 @@ k_attn_combine(int B, int Hq, int Hkv, int nb_max, const int32_t* __restrict__ n
   const int RB = B * G;
   const int nb = min(max(*nb_ptr, 0), nb_max);
   const int g = blockIdx.y;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= nb * RB) return;
-  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (r >= nb * RB) return;   // whole half-waves: a row's 32 lanes leave together
+  const int l = threadIdx.x & 31;
+  const int half = threadIdx.x & 32;   // lane offset of this row's half of the wave
   const size_t rmax = static_cast<size_t>(nb_max) * RB;
   const float* pm = part + static_cast<size_t>(splits) * Hkv * rmax * kAD;
   const float* pl = pm + static_cast<size_t>(splits) * Hkv * rmax;
-  // lane s < splits holds split s's (max, sum)
-  const size_t lrow = (static_cast<size_t>(min(lane, splits - 1)) * Hkv + g) * rmax + r;
-  const float ms = lane < splits ? pm[lrow] : -INFINITY;
-  const float ls = lane < splits ? pl[lrow] : 0.f;
-  float2 ov[S];
+  // lane s < splits of the half holds split s's (max, sum)
+  const size_t lrow = (static_cast<size_t>(min(l, splits - 1)) * Hkv + g) * rmax + r;
+  const float ms = l < splits ? pm[lrow] : -INFINITY;
+  const float ls = l < splits ? pl[lrow] : 0.f;
+  f32x4 ov[S];
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    ov[s] = *reinterpret_cast<const float2*>(
-          part + ((static_cast<size_t>(s) * Hkv + g) * rmax + r) * kAD + 2 * lane);
+    ov[s] = *reinterpret_cast<const f32x4*>(
+        part + ((static_cast<size_t>(s) * Hkv + g) * rmax + r) * kAD + 4 * l);
   float M = ms;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-  const float wgt = lane < splits ? exp2f(ms - M) : 0.f;   // 0 for a split that saw no key
-  const float lsum = wave_sum(wgt * ls);
-  float o0 = 0.f, o1 = 0.f;
+  for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  const float wgt = l < splits ? exp2f(ms - M) : 0.f;   // 0 for a split that saw no key
+  float lsum = wgt * ls;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const float ws = __shfl(wgt, s, kWave);
-    o0 += ws * ov[s].x;
-    o1 += ws * ov[s].y;
-  }
+  for (int o = 16; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, kWave);
+  f32x4 acc = f32x4{};
+#pragma unroll
+  for (int s = 0; s < S; ++s) acc += __shfl(wgt, half + s, kWave) * ov[s];
   const float inv = 1.f / lsum;
   const int b = r / RB, rem = r % RB;
   const size_t hoff = (static_cast<size_t>(b * B + rem / G) * Hq + g * G + rem % G) * kAD;
-  const unsigned v = f32_to_bf16_bits(o0 * inv) | (static_cast<unsigned>(f32_to_bf16_bits(o1 * inv)) << 16);
-  *reinterpret_cast<unsigned*>(H + hoff + 2 * lane) = v;
+  const unsigned lo = f32_to_bf16_bits(acc[0] * inv) |
+                      (static_cast<unsigned>(f32_to_bf16_bits(acc[1] * inv)) << 16);
+  const unsigned hi = f32_to_bf16_bits(acc[2] * inv) |
+                      (static_cast<unsigned>(f32_to_bf16_bits(acc[3] * inv)) << 16);
+  *reinterpret_cast<uint2*>(H + hoff + 4 * l) = make_uint2(lo, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,7 +905,7 @@ extern "C" int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const voi
     LOPA_LAUNCH_CHECK();
     if (p.splits > 1) {
       const int rows = nb_max * dims->B * (dims->Hq / dims->Hkv);
-      const dim3 cg((rows + 3) / 4, dims->Hkv);
+      const dim3 cg((rows + 7) / 8, dims->Hkv);
       const float* pw = static_cast<const float*>(ws);
       unsigned short* Hw = static_cast<unsigned short*>(H);
       switch (p.splits) {
