@@ -30,8 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
-# HBM bytes per lopa_lmhead_conf call (k_lmhead_mfma or k_lmhead_wide with
-# k_lmhead_hfrag, + k_lmhead_merge) and per lopa_branch_attn call (k_attn_dma or k_attn_wide +
+# HBM bytes per lopa_lmhead_conf call (k_lmhead_mfma, + k_lmhead_wide where it
+# serves, + k_lmhead_merge) and per lopa_branch_attn call (k_attn_dma or k_attn_wide +
 # k_attn_combine) from two rocprofv3 --pmc runs of this script: FETCH_SIZE x
 # 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are what the same
 # counters read for a 1 GiB device copy).  Keyed by workload and by a hash of
@@ -498,7 +498,7 @@ def head_roofline(cfg, alg, head_us: float) -> dict:
     # pass the bf16 ridge and make it MFMA-bound)
     mfma_bound = (alg["head_flops"] / (BF16_PEAK_TFLOPS * 1e12) >
                   alg["head_bytes"] / (HBM_PEAK_GBS * 1e9))
-    kern = "lopa_lmhead_conf (k_lmhead_mfma, or k_lmhead_hfrag + k_lmhead_wide; + k_lmhead_merge)"
+    kern = "lopa_lmhead_conf (k_lmhead_mfma, + k_lmhead_wide where it serves, + k_lmhead_merge)"
     if mfma_bound:
         return {"kernel": kern, "bound": "mfma", "achieved": round(tflops, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -30,8 +30,8 @@
 //                   names): four waves that load and compute, register
 //                   tiles of up to 13 row tiles, the weight through an LDS
 //                   ring, the activation fragments straight into registers
-//                   from an operand-ordered copy that k_lmhead_hfrag makes
-//                   first.
+//                   from an operand-ordered copy that the narrow kernel's
+//                   launch makes first (it serves no rows then).
 //   k_lmhead_f32    float32: v_mfma_f32_32x32x2_f32 tiles of 256 vocabulary
 //                   entries x 32 rows, staged through LDS.
 //   k_lmhead_plain  bf16 shapes outside the MFMA kernels (hidden not a
@@ -498,14 +498,40 @@ __device__ __forceinline__ void head_body(int V, int hidden, int nparts, int par
   }
 }
 
+// The activation rows in MFMA operand order, for the wide kernel: fragment
+// f = tile * (hidden / 16) + s holds, for lane l, the eight values
+// 16 s + 8 (l / 32) .. +8 of listed row 32 tile + l % 32 (rows past the
+// listed count repeat the last one), 16 bytes per lane, 1 KB per fragment.
+// A wave of the wide kernel then loads its activation fragments straight into
+// registers, each one 1 KB contiguous read from L2.  Wave `wave` of `waves`
+// writes fragments wave, wave + waves, ...
+__device__ __forceinline__ void operand_copy(int M, int hidden, int h_bytes,
+                                             const unsigned short* __restrict__ H,
+                                             const int32_t* __restrict__ rows,
+                                             u32x4* __restrict__ Hf, int wave, int waves) {
+  const int nks = hidden >> 4;
+  const int nfrag = (M + 31) / 32 * nks;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t hr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
+  for (int f = wave; f < nfrag; f += waves) {
+    const int tile = f / nks;
+    const int s = f - tile * nks;
+    const int r = rows[min(tile * 32 + (lane & 31), M - 1)];
+    Hf[static_cast<size_t>(f) * 64 + lane] =
+        __builtin_amdgcn_raw_buffer_load_b128(hr, r * hidden * 2 + s * 32 + (lane >> 5) * 16, 0, 0);
+  }
+}
+
 // kHeadParts workgroups of 768 threads, one per compute unit.  Block b sits
 // on XCD b % 8; the row groups of one vocabulary part take consecutive
 // blocks of the same XCD, so they stream the same weight lines together and
 // the second reader is served from that XCD's L2 (or the MALL behind it).
 // MODE: conf only, + entropy term, or temperature sampling (ws_t then
 // holds the perturbed best score, ws_z the scaled logit of the sample).
-// wide: the wide kernel is launched beside this one and serves the row
-// counts wide_takes() names.
+// wide: the wide kernel is launched after this one and serves the row counts
+// wide_takes() names; for those this launch only writes the wide kernel's
+// operand-ordered copy of the rows (hf).
 template <int MODE>
 __global__ void __launch_bounds__(kHeadThreads)
 k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
@@ -513,10 +539,17 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
               const int32_t* __restrict__ rows, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ nb_ptr, float* __restrict__ ws_m,
               float* __restrict__ ws_s, int32_t* __restrict__ ws_i, float* __restrict__ ws_t,
-              float* __restrict__ ws_z, const Sampling smp, float* __restrict__ logits_out) {
+              float* __restrict__ ws_z, const Sampling smp, float* __restrict__ logits_out,
+              u32x4* __restrict__ hf) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHeadSmem];
   const int M = __builtin_amdgcn_readfirstlane(listed_rows(row_ptr, nb_ptr, nb_max, m_max));
-  if (M <= 0 || (wide && wide_takes(M))) return;
+  if (M <= 0) return;
+  if (wide && wide_takes(M)) {
+    operand_copy(M, hidden, h_bytes, H, rows, hf,
+                 blockIdx.x * (kHeadThreads / 64) + (threadIdx.x >> 6),
+                 gridDim.x * (kHeadThreads / 64));
+    return;
+  }
   const HeadGroups g = head_groups(M);
   const int b = blockIdx.x;
   const int q = b >> 3;
@@ -551,10 +584,11 @@ k_lmhead_mfma(int V, int hidden, int nb_max, int m_max, int wide, int h_bytes,
 // as many as the LDS and the vector-memory counter allow), every wave
 // issuing its share of the buffer loads that write LDS; each weight fragment
 // read from LDS feeds q MFMAs.  The activation rows do not pass through LDS:
-// k_lmhead_hfrag first lays the listed rows out in MFMA operand order (one
-// 1 KB block per 32-row tile and 16-wide K step), and each wave loads its own
-// fragments from there straight into registers, one contiguous 1 KB read per
-// fragment, a chunk ahead (two register sets).  Staging them through LDS as
+// the narrow kernel's launch (which serves no rows then) first lays the
+// listed rows out in MFMA operand order (one 1 KB block per 32-row tile and
+// 16-wide K step), and each wave loads its own fragments from there straight
+// into registers, one contiguous 1 KB read per fragment, four to seven K
+// steps ahead in a ring of eight register sets.  Staging them through LDS as
 // well (the layout before this one: two activation stages, each wave reading
 // 9 fragments per 13 MFMAs) took 460-475 us per call at 13 tiles against
 // 420-430 us here (same box).
@@ -726,32 +760,6 @@ struct LoadCursor {
     }
   }
 };
-
-// The activation rows in MFMA operand order, made once per call for the wide
-// kernel: fragment f = tile * (hidden / 16) + s holds, for lane l, the eight
-// values 16 s + 8 (l / 32) .. +8 of listed row 32 tile + l % 32 (rows past
-// the listed count repeat the last one), 16 bytes per lane, 1 KB per
-// fragment.  A wave then loads its activation fragments straight into
-// registers, each one 1 KB contiguous read from L2.
-__global__ void __launch_bounds__(256)
-k_lmhead_hfrag(int hidden, int nb_max, int m_max, int h_bytes,
-               const unsigned short* __restrict__ H, const int32_t* __restrict__ rows,
-               const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ nb_ptr,
-               u32x4* __restrict__ Hf) {
-  const int M = listed_rows(row_ptr, nb_ptr, nb_max, m_max);
-  if (!wide_takes(M)) return;
-  const int nks = hidden >> 4;
-  const int f = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int tile = f / nks;
-  if (tile * 32 >= M) return;
-  const int lane = threadIdx.x & 63;
-  const int s = f - tile * nks;
-  const int r = rows[min(tile * 32 + (lane & 31), M - 1)];
-  const __amdgpu_buffer_rsrc_t hr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(H), 0, h_bytes, 0x00020000);
-  Hf[static_cast<size_t>(f) * 64 + lane] =
-      __builtin_amdgcn_raw_buffer_load_b128(hr, r * hidden * 2 + s * 32 + (lane >> 5) * 16, 0, 0);
-}
 
 // Bytes of the operand-ordered activation copy for m_max rows.
 __host__ __device__ inline size_t hfrag_bytes(int m_max, int hidden) {
@@ -1455,25 +1463,21 @@ static int lmhead_launch(const lopa_dims* dims, const void* H, const void* W,
     // returns at once.  Full logits and temperature sampling are served by
     // the narrow kernel only (it takes any row count).
     const bool wide = wide_serves<MODE>(p, hidden, logits_out);
+    // the wide kernel's operand-ordered copy of the rows, after the partial
+    // planes
+    const size_t hf_off = (5 * plane * 4 + 255) / 256 * 256;
+    u32x4* hf = wide ? reinterpret_cast<u32x4*>(static_cast<char*>(ws) + hf_off) : nullptr;
     hipLaunchKernelGGL(k_lmhead_mfma<MODE>, dim3(kHeadParts), dim3(kHeadThreads), 0, stream, V,
                        hidden, nb_max, p.m_max, wide ? 1 : 0, h_bytes, Hb, Wb, rows, row_ptr, nb,
-                       wm, wsum, wi, wt, wz, smp, logits_out);
+                       wm, wsum, wi, wt, wz, smp, logits_out, hf);
     LOPA_LAUNCH_CHECK();
     if constexpr (MODE != kModeSample) {
-      if (wide) {
-        // the activation rows in operand order, after the partial planes
-        const size_t hf_off = (5 * plane * 4 + 255) / 256 * 256;
-        unsigned short* hf = reinterpret_cast<unsigned short*>(static_cast<char*>(ws) + hf_off);
-        const size_t hfb = hfrag_bytes(p.m_max, hidden);
-        const int nfrag = (p.m_max + 31) / 32 * (hidden / 16);
-        hipLaunchKernelGGL(k_lmhead_hfrag, dim3((nfrag + 3) / 4), dim3(256), 0, stream, hidden,
-                           nb_max, p.m_max, h_bytes, Hb, rows, row_ptr, nb,
-                           reinterpret_cast<u32x4*>(hf));
-        LOPA_LAUNCH_CHECK();
+      if (wide)
         hipLaunchKernelGGL(k_lmhead_wide<MODE>, dim3(kHeadParts), dim3(kWideThreads), 0, stream,
-                           V, hidden, nb_max, p.m_max, static_cast<int>(hfb), hf, Wb, rows,
-                           row_ptr, nb, wm, wsum, wi, wt, wz, smp);
-      }
+                           V, hidden, nb_max, p.m_max,
+                           static_cast<int>(hfrag_bytes(p.m_max, hidden)),
+                           reinterpret_cast<const unsigned short*>(hf), Wb, rows, row_ptr, nb, wm,
+                           wsum, wi, wt, wz, smp);
     }
   } else {
     const dim3 grid(p.ntiles, p.m_max);
