@@ -40,16 +40,16 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 HEAD_SOURCES = ("lmhead.hip", "head_plan.hpp", "stream_tile.hpp", "lopa_common.hpp")
 ATTN_SOURCES = ("attn.hip", "attn_plan.hpp", "lopa_common.hpp")
 HEAD_TRAFFIC = {
-    "7b-bf16-L512-B32-m24-k4": ("f87d9b2fcb95d115", 1104605110),
-    "7b-bf16-L2048-B32-m28-k8": ("f87d9b2fcb95d115", 1111029384),
-    "7b-bf16-L1024-B32-m24-k15": ("f87d9b2fcb95d115", 1131285813),
-    "7b-bf16-L4096-B64-m48-k8": ("f87d9b2fcb95d115", 1136938159),
+    "7b-bf16-L512-B32-m24-k4": ("31b4d9616e416850", 1104627674),
+    "7b-bf16-L2048-B32-m28-k8": ("31b4d9616e416850", 1111034330),
+    "7b-bf16-L1024-B32-m24-k15": ("31b4d9616e416850", 1131087997),
+    "7b-bf16-L4096-B64-m48-k8": ("31b4d9616e416850", 1136817484),
 }
 ATTN_TRAFFIC = {
-    "7b-bf16-L512-B32-m24-k4": ("b83e9d0f5e96b081", 26936320),
-    "7b-bf16-L2048-B32-m28-k8": ("b83e9d0f5e96b081", 58028288),
-    "7b-bf16-L1024-B32-m24-k15": ("b83e9d0f5e96b081", 28515328),
-    "7b-bf16-L4096-B64-m48-k8": ("b83e9d0f5e96b081", 57835008),
+    "7b-bf16-L512-B32-m24-k4": ("63b58100ea765173", 26504587),
+    "7b-bf16-L2048-B32-m28-k8": ("63b58100ea765173", 57528880),
+    "7b-bf16-L1024-B32-m24-k15": ("63b58100ea765173", 28514114),
+    "7b-bf16-L4096-B64-m48-k8": ("63b58100ea765173", 56802098),
 }
 
 
