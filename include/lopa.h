@@ -194,8 +194,8 @@ int lopa_branch_attn(const lopa_dims* dims, const void* Kp, const void* Vp,
  *     logits_out  NULL, or float [nb_max*B][V] indexed like H rows (b*B+p);
  *                 only listed rows written
  *     ws, ws_bytes  device workspace of at least lopa_workspace_bytes()
- * bf16: MFMA products with float32 accumulation; float32: float32 MFMA
- * products (FMA for shapes outside the MFMA kernels).
+ * bf16: MFMA products with float32 accumulation (FMA when Hq*d is not a
+ * multiple of 64); float32: float32 MFMA products.
  */
 int lopa_lmhead_conf(const lopa_dims* dims, const void* H, const void* W,
                      const int32_t* rows, const int32_t* row_ptr,
