@@ -429,6 +429,9 @@ int lopa_model_synth(const lopa_dims* dims, const lopa_model_dims* md, uint64_t 
  *     ws, ws_bytes: at least lopa_model_workspace_bytes().
  * Projections stream each weight once for all rows (MFMA, float32
  * accumulation, split into partial tiles summed by the consumer kernels).
+ * Up to 160 rows (and gate/up weights of at most 5 * 16 gate rows per compute
+ * unit) the gate/up projection instead accumulates over the whole hidden
+ * width per workgroup and writes the SwiGLU activation itself.
  */
 int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims* md,
                         const void* weights, const void* Kp, const void* Vp,

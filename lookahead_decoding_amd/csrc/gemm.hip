@@ -256,4 +256,281 @@ int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short
   return hipGetLastError() == hipSuccess ? LOPA_OK : LOPA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Gate/up projection with the SwiGLU activation in the same kernel (GluView)
+// ---------------------------------------------------------------------------
+// Four producer waves fill a three-stage ring with each K chunk's T weight
+// tiles (tile t: gate rows 16 (b0 + t) .. +15, then the up rows of the same
+// indices) and XT activation tiles; compute wave w multiplies weight tile w
+// with every activation tile, and a fifth weight tile is shared out by
+// activation tile (wave w takes tiles w and w + 4).  After the last chunk the
+// lane holding gate row j of 16 activation rows swaps half of them with the
+// lane 16 over, which holds up row j of the same rows, and each lane writes
+// bf16(silu(gate) * up) for its eight.
+constexpr int kGluStages = 4;
+constexpr int kGluThreads = 512;   // 4 compute + 4 producer waves
+constexpr int kGluSmem = kGluStages * (kGluTiles * 32 + kGluRows) * kRB;
+
+// Epilogue of one accumulator tile a of weight tile t against activation
+// tile x.  a[q] = Y[activation row 32 x + 8(q/4) + 4 lh + q%4][weight row ln
+// of tile t]: lanes ln < 16 hold gate index 16 (b0 + t) + ln, lanes ln >= 16
+// the up value of index 16 (b0 + t) + ln - 16.
+__device__ __forceinline__ void glu_finish(const GluView& v, unsigned short* __restrict__ act,
+                                           const f32x16& a, int b0, int t, int x) {
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  const bool gl = ln < 16;
+  const int j = 16 * (b0 + t) + (ln & 15);
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const float mine = gl ? a[h] : a[8 + h];
+    const float other = __shfl_xor(gl ? a[8 + h] : a[h], 16, kWave);
+    const float gt = gl ? mine : other;
+    const float up = gl ? other : mine;
+    const int q = gl ? h : 8 + h;
+    const int r = 32 * x + 8 * (q >> 2) + 4 * lh + (q & 3);
+    if (r < v.M)
+      act[static_cast<size_t>(r) * v.inter + j] = f32_to_bf16_bits(gt / (1.f + expf(-gt)) * up);
+  }
+}
+
+// A compute wave with a fixed share of a T x XT tile grid: the (weight tile,
+// activation tile) pairs of [A0, A1) x [C0, C1) and [D0, D1) x [E0, E1).  Per
+// K step it reads the fragments of the weight tiles [WL, WH) and activation
+// tiles [XL, XH) spanning both rectangles once, so a wave with a 2 x 3 block
+// reads 5 fragments for 6 products.
+template <int T, int XT, int A0, int A1, int C0, int C1, int D0, int D1, int E0, int E1>
+__device__ __forceinline__ void glu_role(const GluView& v, unsigned short* __restrict__ act,
+                                         const unsigned char* smem, int b0, int nch) {
+  constexpr int S = kGluStages;
+  constexpr int WR = 32 * T;
+  constexpr int BUF = (WR + 32 * XT) * kRB;
+  constexpr int KS = kKC / 16;
+  constexpr bool HD = D1 > D0 && E1 > E0;
+  constexpr int WL = HD && D0 < A0 ? D0 : A0, WH = HD && D1 > A1 ? D1 : A1;
+  constexpr int XL = HD && E0 < C0 ? E0 : C0, XH = HD && E1 > C1 ? E1 : C1;
+  constexpr int NW = WH - WL, NXT = XH - XL;
+  static_assert(WL >= 0 && WH <= T && XL >= 0 && XH <= XT, "glu role");
+  auto in = [](int t, int x) {
+    return (t >= A0 && t < A1 && x >= C0 && x < C1) || (HD && t >= D0 && t < D1 && x >= E0 && x < E1);
+  };
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  f32x16 acc[NW][NXT];
+#pragma unroll
+  for (int t = 0; t < NW; ++t)
+#pragma unroll
+    for (int x = 0; x < NXT; ++x) acc[t][x] = f32x16{};
+  auto frags = [&](const unsigned char* base, int j, u16x8 (&wf)[NW], u16x8 (&hf)[NXT])
+      __attribute__((always_inline)) {
+    const int s = 2 * j + lh;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      const int r = 32 * (WL + t) + ln;
+      wf[t] = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
+    }
+#pragma unroll
+    for (int x = 0; x < NXT; ++x) {
+      const int r = 32 * (XL + x) + ln;
+      hf[x] = *reinterpret_cast<const u16x8*>(base + (WR + r) * kRB + swz<kKC>(r, s) * 16);
+    }
+  };
+  for (int i = 0; i < nch; ++i) {
+    __syncthreads();
+    const unsigned char* base = smem + (i % S) * BUF;
+    // fragments two K steps ahead of the products
+    u16x8 wf[3][NW], hf[3][NXT];
+    frags(base, 0, wf[0], hf[0]);
+    frags(base, 1, wf[1], hf[1]);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (j + 2 < KS) frags(base, j + 2, wf[(j + 2) % 3], hf[(j + 2) % 3]);
+#pragma unroll
+      for (int t = 0; t < NW; ++t)
+#pragma unroll
+        for (int x = 0; x < NXT; ++x)
+          if (in(WL + t, XL + x))
+            acc[t][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, hf[j % 3][x]), __builtin_bit_cast(bf16x8, wf[j % 3][t]),
+                acc[t][x], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NW; ++t)
+#pragma unroll
+    for (int x = 0; x < NXT; ++x)
+      if (in(WL + t, XL + x)) glu_finish(v, act, acc[t][x], b0, WL + t, XL + x);
+}
+
+template <int XT, int T>
+__device__ __forceinline__ void glu_body(const GluView& v, const unsigned short* __restrict__ X,
+                                         const unsigned short* __restrict__ W,
+                                         unsigned short* __restrict__ act, unsigned char* smem,
+                                         int b0) {
+  constexpr int S = kGluStages;
+  constexpr int WR = 32 * T;                       // weight rows per stage
+  constexpr int BUF = (WR + 32 * XT) * kRB;        // bytes per stage
+  constexpr int KS = kKC / 16;
+  constexpr int EX = T == 5 ? (XT + 3) / 4 : 0;    // shares of the fifth tile per wave
+  static_assert(XT >= 1 && 32 * XT <= kGluRows && T >= 1 && T <= kGluTiles, "glu shape");
+  static_assert(S * BUF <= kGluSmem, "glu stage size");
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int row_bytes = v.K * 2;
+  const int nch = v.K / kKC;
+
+  if (w >= 4) {
+    // ---------------- producer waves ----------------
+    const int pw = w - 4;
+    const int r8 = lane >> 3;
+    const int ls = (lane & 7) ^ r8 ^ (pw & 1);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(W), 0, 2 * v.inter * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(X), 0, v.M * row_bytes, 0x00020000);
+    // row 8 pw + r8 of every weight tile: a gate row for pw < 2, else an up row
+    const int wv = ((pw >= 2 ? v.inter : 0) + 16 * b0 + 8 * (pw & 1) + r8) * row_bytes + ls * 16;
+    // chunk j into stage j % S; past the last chunk, the last is loaded again
+    auto issue = [&](int j) __attribute__((always_inline)) {
+      unsigned char* dst = smem + (j % S) * BUF;
+      const int kc = min(j, nch - 1);
+#pragma unroll
+      for (int p = 0; p < T; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, LOPA_LDS(dst + (4 * p + pw) * 1024), 16, wv,
+                                                 16 * p * row_bytes + kc * kRB, 0, kWeightAux);
+#pragma unroll
+      for (int p = 0; p < XT; ++p) {
+        const int row = min(8 * (4 * p + pw) + r8, v.M - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, LOPA_LDS(dst + WR * kRB + (4 * p + pw) * 1024),
+                                                 16, row * row_bytes + ls * 16, kc * kRB, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) issue(u);
+    wait_vmcnt<(S - 2) * (T + XT)>();
+    __builtin_amdgcn_s_barrier();
+    for (int i = 0; i + 1 < nch; ++i) {
+      issue(i + S - 1);
+      wait_vmcnt<(S - 2) * (T + XT)>();
+      __builtin_amdgcn_s_barrier();
+    }
+    wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+    return;
+  }
+  // ---------------- compute waves ----------------
+  if constexpr (T == 5 && XT == 5) {
+    // 25 products in four blocks of 6, 6, 6 and 7 (5, 5, 5, 7 fragments per
+    // step instead of 8 each with the fifth tile shared out)
+    switch (w) {
+      case 0: glu_role<T, XT, 0, 2, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 1: glu_role<T, XT, 2, 4, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 2: glu_role<T, XT, 0, 3, 3, 5, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      default: glu_role<T, XT, 3, 5, 3, 5, 4, 5, 0, 3>(v, act, smem, b0, nch); break;
+    }
+    return;
+  }
+  if (w >= T) {   // fewer than four tiles: this wave only keeps step
+    for (int i = 0; i < nch; ++i) __syncthreads();
+    return;
+  }
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  f32x16 acc[XT], ext[EX > 0 ? EX : 1];
+#pragma unroll
+  for (int x = 0; x < XT; ++x) acc[x] = f32x16{};
+#pragma unroll
+  for (int e = 0; e < (EX > 0 ? EX : 1); ++e) ext[e] = f32x16{};
+  // activation tile of the wave's e-th share of the fifth weight tile
+  auto ext_tile = [&](int e) __attribute__((always_inline)) { return min(w + 4 * e, XT - 1); };
+  auto frags = [&](const unsigned char* base, int j, u16x8& wo, u16x8& w4, u16x8 (&hf)[XT],
+                   u16x8 (&hx)[EX > 0 ? EX : 1]) __attribute__((always_inline)) {
+    const int s = 2 * j + lh;
+    {
+      const int r = 32 * w + ln;
+      wo = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
+    }
+    if constexpr (T == 5) {
+      const int r = 128 + ln;
+      w4 = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
+#pragma unroll
+      for (int e = 0; e < EX; ++e) {
+        const int rx = 32 * ext_tile(e) + ln;
+        hx[e] = *reinterpret_cast<const u16x8*>(base + (WR + rx) * kRB + swz<kKC>(rx, s) * 16);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < XT; ++x) {
+      const int r = 32 * x + ln;
+      hf[x] = *reinterpret_cast<const u16x8*>(base + (WR + r) * kRB + swz<kKC>(r, s) * 16);
+    }
+  };
+  for (int i = 0; i < nch; ++i) {
+    __syncthreads();
+    const unsigned char* base = smem + (i % S) * BUF;
+    // fragments two K steps ahead of the products
+    u16x8 wo[3], w4[3], hf[3][XT], hx[3][EX > 0 ? EX : 1];
+    frags(base, 0, wo[0], w4[0], hf[0], hx[0]);
+    frags(base, 1, wo[1], w4[1], hf[1], hx[1]);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (j + 2 < KS)
+        frags(base, j + 2, wo[(j + 2) % 3], w4[(j + 2) % 3], hf[(j + 2) % 3], hx[(j + 2) % 3]);
+#pragma unroll
+      for (int x = 0; x < XT; ++x)
+        acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hf[j % 3][x]),
+                                                         __builtin_bit_cast(bf16x8, wo[j % 3]),
+                                                         acc[x], 0, 0, 0);
+      if constexpr (T == 5) {
+#pragma unroll
+        for (int e = 0; e < EX; ++e)
+          ext[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, hx[j % 3][e]), __builtin_bit_cast(bf16x8, w4[j % 3]),
+              ext[e], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < XT; ++x) glu_finish(v, act, acc[x], b0, w, x);
+  if constexpr (T == 5) {
+#pragma unroll
+    for (int e = 0; e < EX; ++e)
+      if (w + 4 * e < XT) glu_finish(v, act, ext[e], b0, 4, w + 4 * e);
+  }
+}
+
+template <int XT>
+__global__ void __launch_bounds__(kGluThreads)
+k_gemm_glu(GluView v, const unsigned short* __restrict__ X, const unsigned short* __restrict__ W,
+           unsigned short* __restrict__ act) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kGluSmem];
+  const int b0 = v.blk_begin(blockIdx.x);
+  const int T = v.blk_begin(blockIdx.x + 1) - b0;
+  switch (T) {
+    case 1: glu_body<XT, 1>(v, X, W, act, smem, b0); break;
+    case 2: glu_body<XT, 2>(v, X, W, act, smem, b0); break;
+    case 3: glu_body<XT, 3>(v, X, W, act, smem, b0); break;
+    case 4: glu_body<XT, 4>(v, X, W, act, smem, b0); break;
+    case 5: glu_body<XT, 5>(v, X, W, act, smem, b0); break;
+    default: break;   // the plan keeps T in 1 .. kGluTiles
+  }
+}
+
+// Enqueue act = bf16(silu(X Wg^T) * (X Wu^T)) for W = [gate rows; up rows].
+int glu_launch(const GluView& v, const unsigned short* X, const unsigned short* W,
+               unsigned short* act, hipStream_t stream) {
+  const dim3 grid(v.G), block(kGluThreads);
+  switch ((v.M + 31) / 32) {
+    case 1: hipLaunchKernelGGL(k_gemm_glu<1>, grid, block, 0, stream, v, X, W, act); break;
+    case 2: hipLaunchKernelGGL(k_gemm_glu<2>, grid, block, 0, stream, v, X, W, act); break;
+    case 3: hipLaunchKernelGGL(k_gemm_glu<3>, grid, block, 0, stream, v, X, W, act); break;
+    case 4: hipLaunchKernelGGL(k_gemm_glu<4>, grid, block, 0, stream, v, X, W, act); break;
+    case 5: hipLaunchKernelGGL(k_gemm_glu<5>, grid, block, 0, stream, v, X, W, act); break;
+    default: return LOPA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? LOPA_OK : LOPA_ERR_HIP;
+}
+
 }  // namespace lopa

@@ -131,4 +131,41 @@ inline GemmView gemm_view(int M, int N, int K, int max_wgs = kGemmMaxWorkgroups)
   return v;
 }
 
+// Gate/up projection of the MLP with its SwiGLU finished in the same kernel
+// (k_gemm_glu): workgroup g takes blocks [blk_begin(g), blk_begin(g + 1)) of
+// 16 gate rows and the 16 up rows of the same indices, one 32-row weight
+// tile per block, over the whole of K, so no partial tiles are written and
+// no second kernel sums them.  At most kGluTiles blocks per workgroup and
+// kGluRows activation rows (one 160-row group); other shapes take the
+// stream-K GEMM and k_swiglu.
+constexpr int kGluTiles = 5;
+constexpr int kGluRows = 160;
+
+struct GluView {
+  int M, K, inter;
+  int nblk;   // inter / 16
+  int G;      // workgroups
+  __host__ __device__ int blk_begin(int g) const {
+    return static_cast<int>(static_cast<long long>(g) * nblk / G);
+  }
+};
+
+inline bool glu_fits(int M, int K, int inter) {
+  if (M < 1 || M > kGluRows || K % 64 != 0 || inter % 16 != 0 || inter < 16) return false;
+  const int nblk = inter / 16;
+  const int G = nblk < kGemmMaxWorkgroups ? nblk : kGemmMaxWorkgroups;
+  // buffer offsets of the weight (2 inter rows of K bf16) stay below 2^31
+  return (nblk + G - 1) / G <= kGluTiles && 4LL * inter * K < (1LL << 31);
+}
+
+inline GluView glu_view(int M, int K, int inter) {
+  GluView v{};
+  v.M = M;
+  v.K = K;
+  v.inter = inter;
+  v.nblk = inter / 16;
+  v.G = v.nblk < kGemmMaxWorkgroups ? v.nblk : kGemmMaxWorkgroups;
+  return v;
+}
+
 }  // namespace lopa

@@ -24,6 +24,8 @@ namespace lopa {
 
 int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short* W, float* P,
                 hipStream_t stream);
+int glu_launch(const GluView& v, const unsigned short* X, const unsigned short* W,
+               unsigned short* act, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Synthetic weights
@@ -451,11 +453,15 @@ extern "C" int lopa_branch_forward(const lopa_dims* dims, const lopa_model_dims*
                        wt(lb + lay.mlp_norm), x, h);
     LOPA_LAUNCH_CHECK();
     // MLP block
-    if ((st = gemm_launch(gm.gu, h, wt(lb + lay.wgu), P, stream)) != LOPA_OK) return st;
-    const long long na = static_cast<long long>(M) * (s.inter / 4);
-    hipLaunchKernelGGL(k_swiglu, dim3(static_cast<unsigned>((na + 255) / 256)), dim3(256), 0,
-                       stream, gm.gu, P, s.inter, act);
-    LOPA_LAUNCH_CHECK();
+    if (gm.glu_on) {
+      if ((st = glu_launch(gm.glu, h, wt(lb + lay.wgu), act, stream)) != LOPA_OK) return st;
+    } else {
+      if ((st = gemm_launch(gm.gu, h, wt(lb + lay.wgu), P, stream)) != LOPA_OK) return st;
+      const long long na = static_cast<long long>(M) * (s.inter / 4);
+      hipLaunchKernelGGL(k_swiglu, dim3(static_cast<unsigned>((na + 255) / 256)), dim3(256), 0,
+                         stream, gm.gu, P, s.inter, act);
+      LOPA_LAUNCH_CHECK();
+    }
     if ((st = gemm_launch(gm.down, act, wt(lb + lay.wd), P, stream)) != LOPA_OK) return st;
     const bool last = l + 1 == md->n_layers;
     const unsigned short* gnext =

@@ -53,12 +53,16 @@ inline lopa_model_layout model_layout(const lopa_dims& d, const lopa_model_dims&
 }
 
 // The four projections of one layer, in order: q/k/v, output, gate+up, down.
+// Where the shape allows (glu_on), gate+up and its SwiGLU run as one kernel
+// over the GluView and write no partial tiles.
 struct LayerGemms {
   GemmView qkv, o, gu, down;
+  GluView glu;
+  bool glu_on;
   size_t partial_bytes() const {
     size_t b = qkv.partial_bytes();
     if (o.partial_bytes() > b) b = o.partial_bytes();
-    if (gu.partial_bytes() > b) b = gu.partial_bytes();
+    if (!glu_on && gu.partial_bytes() > b) b = gu.partial_bytes();
     if (down.partial_bytes() > b) b = down.partial_bytes();
     return b;
   }
@@ -93,6 +97,8 @@ inline LayerGemms layer_gemms(const lopa_dims& d, const lopa_model_dims& md) {
   g.qkv = five ? aligned_view(s.M, s.qkv, s.hidden, 4) : gemm_view(s.M, s.qkv, s.hidden);
   g.o = five ? aligned_view(s.M, s.hidden, s.hq_d, 4) : gemm_view(s.M, s.hidden, s.hq_d);
   g.gu = gemm_view(s.M, 2 * s.inter, s.hidden);
+  g.glu_on = glu_fits(s.M, s.hidden, s.inter);
+  g.glu = glu_view(s.M, s.hidden, s.inter);
   g.down = five ? aligned_view(s.M, s.hidden, s.inter, 8) : gemm_view(s.M, s.hidden, s.inter);
   return g;
 }

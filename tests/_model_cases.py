@@ -21,6 +21,12 @@ FWD_CASES = [
     # 144 rows: the 160-row projection tile with 16 padding rows
     ("tile160-M144", dict(L=50, B=48, k_max=2, Hq=4, Hkv=2, d=64, inter=512, V=800,
                           n_layers=2), 3),
+    # gate/up with its SwiGLU in one kernel: the 7B model's 18944-wide MLP
+    # gives four and five weight tiles per workgroup, 10240 two and three
+    ("glu-tiles4-5-M160", dict(L=32, B=32, k_max=4, Hq=4, Hkv=2, d=64, inter=18944, V=600,
+                               n_layers=1), 5),
+    ("glu-tiles2-3-M72", dict(L=20, B=24, k_max=2, Hq=2, Hkv=1, d=64, inter=10240, V=300,
+                              n_layers=1), 3),
     # the 7B model's depth at a small width: errors compounding over 28 layers
     ("deep-28-layers", dict(L=40, B=16, k_max=3, Hq=4, Hkv=2, d=64, inter=512, V=1000,
                             n_layers=28), 4),
