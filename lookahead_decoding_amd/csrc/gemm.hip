@@ -268,7 +268,7 @@ int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short
 // lane 16 over, which holds up row j of the same rows, and each lane writes
 // bf16(silu(gate) * up) for its eight.
 constexpr int kGluStages = 4;
-constexpr int kGluThreads = 512;   // 4 compute + 4 producer waves
+constexpr int kGluThreads = 768;   // 8 compute + 4 producer waves
 constexpr int kGluSmem = kGluStages * (kGluTiles * 32 + kGluRows) * kRB;
 
 // Epilogue of one accumulator tile a of weight tile t against activation
@@ -373,7 +373,6 @@ __device__ __forceinline__ void glu_body(const GluView& v, const unsigned short*
   constexpr int WR = 32 * T;                       // weight rows per stage
   constexpr int BUF = (WR + 32 * XT) * kRB;        // bytes per stage
   constexpr int KS = kKC / 16;
-  constexpr int EX = T == 5 ? (XT + 3) / 4 : 0;    // shares of the fifth tile per wave
   static_assert(XT >= 1 && 32 * XT <= kGluRows && T >= 1 && T <= kGluTiles, "glu shape");
   static_assert(S * BUF <= kGluSmem, "glu stage size");
   const int tid = threadIdx.x;
@@ -382,9 +381,9 @@ __device__ __forceinline__ void glu_body(const GluView& v, const unsigned short*
   const int row_bytes = v.K * 2;
   const int nch = v.K / kKC;
 
-  if (w >= 4) {
+  if (w >= 8) {
     // ---------------- producer waves ----------------
-    const int pw = w - 4;
+    const int pw = w - 8;
     const int r8 = lane >> 3;
     const int ls = (lane & 7) ^ r8 ^ (pw & 1);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -421,45 +420,50 @@ __device__ __forceinline__ void glu_body(const GluView& v, const unsigned short*
     return;
   }
   // ---------------- compute waves ----------------
-  if constexpr (T == 5 && XT == 5) {
-    // 25 products in four blocks of 6, 6, 6 and 7 (5, 5, 5, 7 fragments per
-    // step instead of 8 each with the fifth tile shared out)
+  if constexpr (XT == 5 && (T == 5 || T == 4)) {
+    // 2-D blocks of the T x 5 tile grid over the eight waves; waves w and
+    // w + 4 share a SIMD: with T = 5 the SIMDs carry 7, 6, 6, 6 products per
+    // step (4 + 3, 4 + 2, ...), with T = 4 five each
     switch (w) {
-      case 0: glu_role<T, XT, 0, 2, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      case 1: glu_role<T, XT, 2, 4, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      case 2: glu_role<T, XT, 0, 3, 3, 5, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      default: glu_role<T, XT, 3, 5, 3, 5, 4, 5, 0, 3>(v, act, smem, b0, nch); break;
+      case 0: glu_role<T, XT, 0, 2, 0, 2, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 1: glu_role<T, XT, 0, 2, 2, 4, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 2: glu_role<T, XT, 2, 4, 0, 2, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 3: glu_role<T, XT, 2, 4, 2, 4, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 4:
+        if constexpr (T == 5) glu_role<T, XT, 4, 5, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 0, 1, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        break;
+      case 5:
+        if constexpr (T == 5) glu_role<T, XT, 4, 5, 3, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 1, 2, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        break;
+      case 6:
+        if constexpr (T == 5) glu_role<T, XT, 0, 2, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 2, 3, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        break;
+      default:
+        if constexpr (T == 5) glu_role<T, XT, 2, 4, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 3, 4, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        break;
     }
     return;
   }
-  if (w >= T) {   // fewer than four tiles: this wave only keeps step
+  if (w >= T) {   // fewer than eight tiles: this wave only keeps step
     for (int i = 0; i < nch; ++i) __syncthreads();
     return;
   }
+  // wave w: weight tile w against every activation tile
   const int ln = lane & 31;
   const int lh = lane >> 5;
-  f32x16 acc[XT], ext[EX > 0 ? EX : 1];
+  f32x16 acc[XT];
 #pragma unroll
   for (int x = 0; x < XT; ++x) acc[x] = f32x16{};
-#pragma unroll
-  for (int e = 0; e < (EX > 0 ? EX : 1); ++e) ext[e] = f32x16{};
-  // activation tile of the wave's e-th share of the fifth weight tile
-  auto ext_tile = [&](int e) __attribute__((always_inline)) { return min(w + 4 * e, XT - 1); };
-  auto frags = [&](const unsigned char* base, int j, u16x8& wo, u16x8& w4, u16x8 (&hf)[XT],
-                   u16x8 (&hx)[EX > 0 ? EX : 1]) __attribute__((always_inline)) {
+  auto frags = [&](const unsigned char* base, int j, u16x8& wo, u16x8 (&hf)[XT])
+      __attribute__((always_inline)) {
     const int s = 2 * j + lh;
     {
       const int r = 32 * w + ln;
       wo = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
-    }
-    if constexpr (T == 5) {
-      const int r = 128 + ln;
-      w4 = *reinterpret_cast<const u16x8*>(base + r * kRB + swz<kKC>(r, s) * 16);
-#pragma unroll
-      for (int e = 0; e < EX; ++e) {
-        const int rx = 32 * ext_tile(e) + ln;
-        hx[e] = *reinterpret_cast<const u16x8*>(base + (WR + rx) * kRB + swz<kKC>(rx, s) * 16);
-      }
     }
 #pragma unroll
     for (int x = 0; x < XT; ++x) {
@@ -471,34 +475,21 @@ __device__ __forceinline__ void glu_body(const GluView& v, const unsigned short*
     __syncthreads();
     const unsigned char* base = smem + (i % S) * BUF;
     // fragments two K steps ahead of the products
-    u16x8 wo[3], w4[3], hf[3][XT], hx[3][EX > 0 ? EX : 1];
-    frags(base, 0, wo[0], w4[0], hf[0], hx[0]);
-    frags(base, 1, wo[1], w4[1], hf[1], hx[1]);
+    u16x8 wo[3], hf[3][XT];
+    frags(base, 0, wo[0], hf[0]);
+    frags(base, 1, wo[1], hf[1]);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      if (j + 2 < KS)
-        frags(base, j + 2, wo[(j + 2) % 3], w4[(j + 2) % 3], hf[(j + 2) % 3], hx[(j + 2) % 3]);
+      if (j + 2 < KS) frags(base, j + 2, wo[(j + 2) % 3], hf[(j + 2) % 3]);
 #pragma unroll
       for (int x = 0; x < XT; ++x)
         acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hf[j % 3][x]),
                                                          __builtin_bit_cast(bf16x8, wo[j % 3]),
                                                          acc[x], 0, 0, 0);
-      if constexpr (T == 5) {
-#pragma unroll
-        for (int e = 0; e < EX; ++e)
-          ext[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, hx[j % 3][e]), __builtin_bit_cast(bf16x8, w4[j % 3]),
-              ext[e], 0, 0, 0);
-      }
     }
   }
 #pragma unroll
   for (int x = 0; x < XT; ++x) glu_finish(v, act, acc[x], b0, w, x);
-  if constexpr (T == 5) {
-#pragma unroll
-    for (int e = 0; e < EX; ++e)
-      if (w + 4 * e < XT) glu_finish(v, act, ext[e], b0, 4, w + 4 * e);
-  }
 }
 
 template <int XT>
