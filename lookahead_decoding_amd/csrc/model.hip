@@ -295,11 +295,14 @@ static int check_model(const lopa_dims* d, const lopa_model_dims* md) {
     return LOPA_ERR_UNSUPPORTED;
   // every projection's units fit the consumers' slot tables
   const lopa::LayerGemms gm = lopa::layer_gemms(*d, *md);
+  // (gate+up has no partial tiles where k_gemm_glu serves it)
+  const bool gu_parts = !gm.glu_on;
   if (gm.qkv.units > lopa::kSlotTableMax || gm.o.units > lopa::kSlotTableMax ||
-      gm.gu.units > lopa::kSlotTableMax || gm.down.units > lopa::kSlotTableMax)
+      (gu_parts && gm.gu.units > lopa::kSlotTableMax) || gm.down.units > lopa::kSlotTableMax)
     return LOPA_ERR_UNSUPPORTED;
   // the consumers' slot table holds one byte per unit
-  if (gm.qkv.smax > 255 || gm.o.smax > 255 || gm.gu.smax > 255 || gm.down.smax > 255)
+  if (gm.qkv.smax > 255 || gm.o.smax > 255 || (gu_parts && gm.gu.smax > 255) ||
+      gm.down.smax > 255)
     return LOPA_ERR_UNSUPPORTED;
   return LOPA_OK;
 }
