@@ -259,13 +259,14 @@ int gemm_launch(const GemmView& v, const unsigned short* X, const unsigned short
 // ---------------------------------------------------------------------------
 // Gate/up projection with the SwiGLU activation in the same kernel (GluView)
 // ---------------------------------------------------------------------------
-// Four producer waves fill a three-stage ring with each K chunk's T weight
+// Four producer waves fill a four-stage ring with each K chunk's T weight
 // tiles (tile t: gate rows 16 (b0 + t) .. +15, then the up rows of the same
-// indices) and XT activation tiles; compute wave w multiplies weight tile w
-// with every activation tile, and a fifth weight tile is shared out by
-// activation tile (wave w takes tiles w and w + 4).  After the last chunk the
-// lane holding gate row j of 16 activation rows swaps half of them with the
-// lane 16 over, which holds up row j of the same rows, and each lane writes
+// indices) and XT activation tiles.  Eight compute waves, two per SIMD: with
+// five activation tiles (129-160 rows) and four or five weight tiles they
+// take 2-D blocks of the tile grid (glu_role), otherwise wave w multiplies
+// weight tile w with every activation tile.  After the last chunk the lane
+// holding gate row j of 16 activation rows swaps half of them with the lane
+// 16 over, which holds up row j of the same rows, and each lane writes
 // bf16(silu(gate) * up) for its eight.
 constexpr int kGluStages = 4;
 constexpr int kGluThreads = 768;   // 8 compute + 4 producer waves
