@@ -27,6 +27,12 @@ FWD_CASES = [
                                n_layers=1), 5),
     ("glu-tiles2-3-M72", dict(L=20, B=24, k_max=2, Hq=2, Hkv=1, d=64, inter=10240, V=300,
                               n_layers=1), 3),
+    # the 2-D wave blocks with padding rows (150 of 160 staged), and four
+    # activation tiles against four or five weight tiles (one wave per tile)
+    ("glu-blocks-M150", dict(L=24, B=30, k_max=4, Hq=4, Hkv=2, d=64, inter=18944, V=400,
+                             n_layers=1), 4),
+    ("glu-tiles4-5-M128", dict(L=16, B=32, k_max=3, Hq=8, Hkv=2, d=64, inter=18944, V=350,
+                               n_layers=1), 4),
     # the 7B model's depth at a small width: errors compounding over 28 layers
     ("deep-28-layers", dict(L=40, B=16, k_max=3, Hq=4, Hkv=2, d=64, inter=512, V=1000,
                             n_layers=28), 4),

@@ -267,3 +267,15 @@ def test_noalloc_head_rejects_before_any_launch():
     assert lopa.workspace_bytes(d) == 1024 * 256 * 20 + 1024 * 7168 * 2
     assert L.lopa_lmhead_conf_noalloc(ctypes.byref(d), *([fake] * 8), None) == -5
     assert "scratch" in lopa.status_string(-5)
+
+def test_forward_cases_are_supported_shapes():
+    """Every geometry the GPU forward tests run is one the library accepts
+    (checked here on the host, before any of them reaches a GPU)."""
+    from _model_cases import FWD_CASES
+    for name, case, _ in FWD_CASES:
+        d = _dims(L=case["L"], B=case["B"], Hq=case["Hq"], Hkv=case["Hkv"], d=case["d"],
+                  V=case["V"], k_max=case["k_max"])
+        md = _model_dims(n_layers=case["n_layers"], inter=case["inter"], mask_id=case["V"] - 1)
+        out = lopa.ModelLayout()
+        assert lopa.lib().lopa_model_layout_of(ctypes.byref(d), ctypes.byref(md),
+                                               ctypes.byref(out)) == 0, name
