@@ -18,7 +18,8 @@ generator) against oracle/model_oracle.py.
   2^-16 (the largest float32-level discrepancy) and records, per case, the
   largest and the mean |difference| / RMS over four draws
   (tests/golden/forward_noise.json).  The GPU must stay within twice the
-  largest and 1.5 times the mean.  Cases: six 1-3 layer geometries, the 7B
+  largest and 1.5 times the mean.  Cases: ten 1-3 layer geometries (four of
+  them for the fused gate/up kernel's tile counts), the 7B
   model's 28 layers at a small width, and the 7B width with 2 layers.
 * A whole step with the model (build -> forward -> LM head -> select): nb,
   rows and the tokens of rows whose top-2 logit gap exceeds 0.05 identical to
