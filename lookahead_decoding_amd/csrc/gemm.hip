@@ -296,26 +296,20 @@ __device__ __forceinline__ void glu_finish(const GluView& v, unsigned short* __r
   }
 }
 
-// A compute wave with a fixed share of a T x XT tile grid: the (weight tile,
-// activation tile) pairs of [A0, A1) x [C0, C1) and [D0, D1) x [E0, E1).  Per
-// K step it reads the fragments of the weight tiles [WL, WH) and activation
-// tiles [XL, XH) spanning both rectangles once, so a wave with a 2 x 3 block
-// reads 5 fragments for 6 products.
-template <int T, int XT, int A0, int A1, int C0, int C1, int D0, int D1, int E0, int E1>
+// A compute wave with a fixed block of a T x XT tile grid: the (weight tile,
+// activation tile) pairs of [A0, A1) x [C0, C1).  Per K step it reads the
+// fragments of those weight and activation tiles once, so a wave with a
+// 2 x 2 block reads 4 fragments for 4 products.
+template <int T, int XT, int A0, int A1, int C0, int C1>
 __device__ __forceinline__ void glu_role(const GluView& v, unsigned short* __restrict__ act,
                                          const unsigned char* smem, int b0, int nch) {
   constexpr int S = kGluStages;
   constexpr int WR = 32 * T;
   constexpr int BUF = (WR + 32 * XT) * kRB;
   constexpr int KS = kKC / 16;
-  constexpr bool HD = D1 > D0 && E1 > E0;
-  constexpr int WL = HD && D0 < A0 ? D0 : A0, WH = HD && D1 > A1 ? D1 : A1;
-  constexpr int XL = HD && E0 < C0 ? E0 : C0, XH = HD && E1 > C1 ? E1 : C1;
+  constexpr int WL = A0, WH = A1, XL = C0, XH = C1;
   constexpr int NW = WH - WL, NXT = XH - XL;
-  static_assert(WL >= 0 && WH <= T && XL >= 0 && XH <= XT, "glu role");
-  auto in = [](int t, int x) {
-    return (t >= A0 && t < A1 && x >= C0 && x < C1) || (HD && t >= D0 && t < D1 && x >= E0 && x < E1);
-  };
+  static_assert(WL >= 0 && WH <= T && XL >= 0 && XH <= XT && NW > 0 && NXT > 0, "glu role");
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31;
   const int lh = lane >> 5;
@@ -352,17 +346,16 @@ __device__ __forceinline__ void glu_role(const GluView& v, unsigned short* __res
       for (int t = 0; t < NW; ++t)
 #pragma unroll
         for (int x = 0; x < NXT; ++x)
-          if (in(WL + t, XL + x))
-            acc[t][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, hf[j % 3][x]), __builtin_bit_cast(bf16x8, wf[j % 3][t]),
-                acc[t][x], 0, 0, 0);
+          acc[t][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, hf[j % 3][x]), __builtin_bit_cast(bf16x8, wf[j % 3][t]),
+              acc[t][x], 0, 0, 0);
     }
   }
 #pragma unroll
   for (int t = 0; t < NW; ++t)
 #pragma unroll
     for (int x = 0; x < NXT; ++x)
-      if (in(WL + t, XL + x)) glu_finish(v, act, acc[t][x], b0, WL + t, XL + x);
+      glu_finish(v, act, acc[t][x], b0, WL + t, XL + x);
 }
 
 template <int XT, int T>
@@ -426,25 +419,25 @@ __device__ __forceinline__ void glu_body(const GluView& v, const unsigned short*
     // w + 4 share a SIMD: with T = 5 the SIMDs carry 7, 6, 6, 6 products per
     // step (4 + 3, 4 + 2, ...), with T = 4 five each
     switch (w) {
-      case 0: glu_role<T, XT, 0, 2, 0, 2, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      case 1: glu_role<T, XT, 0, 2, 2, 4, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      case 2: glu_role<T, XT, 2, 4, 0, 2, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
-      case 3: glu_role<T, XT, 2, 4, 2, 4, 0, 0, 0, 0>(v, act, smem, b0, nch); break;
+      case 0: glu_role<T, XT, 0, 2, 0, 2>(v, act, smem, b0, nch); break;
+      case 1: glu_role<T, XT, 0, 2, 2, 4>(v, act, smem, b0, nch); break;
+      case 2: glu_role<T, XT, 2, 4, 0, 2>(v, act, smem, b0, nch); break;
+      case 3: glu_role<T, XT, 2, 4, 2, 4>(v, act, smem, b0, nch); break;
       case 4:
-        if constexpr (T == 5) glu_role<T, XT, 4, 5, 0, 3, 0, 0, 0, 0>(v, act, smem, b0, nch);
-        else glu_role<T, XT, 0, 1, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        if constexpr (T == 5) glu_role<T, XT, 4, 5, 0, 3>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 0, 1, 4, 5>(v, act, smem, b0, nch);
         break;
       case 5:
-        if constexpr (T == 5) glu_role<T, XT, 4, 5, 3, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
-        else glu_role<T, XT, 1, 2, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        if constexpr (T == 5) glu_role<T, XT, 4, 5, 3, 5>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 1, 2, 4, 5>(v, act, smem, b0, nch);
         break;
       case 6:
-        if constexpr (T == 5) glu_role<T, XT, 0, 2, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
-        else glu_role<T, XT, 2, 3, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        if constexpr (T == 5) glu_role<T, XT, 0, 2, 4, 5>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 2, 3, 4, 5>(v, act, smem, b0, nch);
         break;
       default:
-        if constexpr (T == 5) glu_role<T, XT, 2, 4, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
-        else glu_role<T, XT, 3, 4, 4, 5, 0, 0, 0, 0>(v, act, smem, b0, nch);
+        if constexpr (T == 5) glu_role<T, XT, 2, 4, 4, 5>(v, act, smem, b0, nch);
+        else glu_role<T, XT, 3, 4, 4, 5>(v, act, smem, b0, nch);
         break;
     }
     return;
